@@ -1,0 +1,157 @@
+"""Plain float64 CPU oracle for exact scaled dot-product attention.
+
+TEST INFRASTRUCTURE. Only the test-suite, the package smoke check and the
+benchmark's CPU-baseline leg may import this module. It shares no code with
+the HIP path, and the HIP path never calls it.
+
+Sources (the pages, by title and section):
+  * "FlashAttention" (interactiveprimer), intro and "The bottleneck is memory,
+    not multiplication": attention over N tokens forms the N x N matrix of
+    scaled query-key scores, applies a softmax per query row and multiplies the
+    result by the values; FlashAttention returns exactly that result.
+  * "FlashAttention, simplified", "The trick": the streaming form -- a running
+    row maximum m, a running sum l of exponentials, an accumulator rescaled by
+    exp(m_old - m_new) whenever the maximum grows, and one division by l at the
+    end -- whose output equals standard attention.
+  * "What FlashAttention actually buys", "The actual problem": the tiled result
+    is exact attention, not an approximation.
+
+Readings taken where the pages are silent (each also listed with the design
+notes of this repository):
+  * scale: the scores are ``scale * q_i . k_j`` with ``scale`` a caller value
+    (the pages say "scaled" but give no value); workloads use 1/sqrt(d).
+  * logsumexp: LSE_i = m_i + ln(l_i) in natural log of the scaled scores.  It is
+    not on the pages; it is the per-row state (m, l) reduced to one number.
+  * The streaming loop runs over K/V blocks only: query rows are independent,
+    so all query rows are carried together.
+
+Parity pins: every function here is checked by ``tests/test_oracle_pins.py``
+against brute force in high-precision decimal arithmetic, closed forms,
+invariants and an independent library attention routine; none is "parity
+unpinned".
+"""
+from __future__ import annotations
+
+import numpy as np
+
+# Upper bound on the float64 score block held at once (bytes); complete score
+# rows are always kept, only the number of rows per block changes.
+_BLOCK_BYTES = 1 << 28
+
+
+def _f64(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float64)
+
+
+def _check(q, k, v):
+    if q.ndim < 2 or k.ndim != q.ndim or v.ndim != q.ndim:
+        raise ValueError("q, k, v must have the same rank >= 2")
+    if q.shape[:-2] != k.shape[:-2] or q.shape[:-2] != v.shape[:-2]:
+        raise ValueError("q, k, v leading dimensions differ")
+    if q.shape[-1] != k.shape[-1]:
+        raise ValueError("q and k must share the feature size")
+    if k.shape[-2] != v.shape[-2]:
+        raise ValueError("k and v must have the same number of rows")
+
+
+def attention_reference(q, k, v, scale: float):
+    """Exact attention by its definition, in float64, with complete score rows.
+
+    For each leading index (batch, head) and each query row i:
+        S_ij   = scale * sum_t q_it k_jt            (all N keys of the row)
+        m_i    = max_j S_ij
+        E_ij   = exp(S_ij - m_i),  l_i = sum_j E_ij
+        P_ij   = E_ij / l_i                          (softmax of the row)
+        O_i    = sum_j P_ij v_j
+        LSE_i  = m_i + ln l_i
+    ("FlashAttention" (interactiveprimer), intro: score matrix, softmax, values.)
+
+    q: [..., Nq, d], k: [..., Nk, d], v: [..., Nk, dv]; any real dtype, upcast
+    exactly to float64. ``scale`` is used as the float64 value of the argument.
+    Returns (O float64 [..., Nq, dv], LSE float64 [..., Nq]). Rows are handled
+    in blocks of complete rows, which leaves the row-wise definition unchanged.
+    With Nk == 0 the softmax is undefined and a ValueError is raised.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    _check(q, k, v)
+    lead = q.shape[:-2]
+    nq, nk, dv = q.shape[-2], k.shape[-2], v.shape[-1]
+    if nk == 0 and nq > 0:
+        raise ValueError("softmax over zero keys is undefined")
+    s = np.float64(scale)
+    out = np.empty(lead + (nq, dv), dtype=np.float64)
+    lse = np.empty(lead + (nq,), dtype=np.float64)
+    rows = max(1, _BLOCK_BYTES // max(1, 8 * nk))
+    for idx in np.ndindex(*lead):
+        qh, kh, vh = q[idx], k[idx], v[idx]
+        for r0 in range(0, nq, rows):
+            r1 = min(nq, r0 + rows)
+            scores = s * (qh[r0:r1] @ kh.T)
+            m = scores.max(axis=1)
+            e = np.exp(scores - m[:, None])
+            l = e.sum(axis=1)
+            p = e / l[:, None]
+            out[idx][r0:r1] = p @ vh
+            lse[idx][r0:r1] = m + np.log(l)
+    return out, lse
+
+
+def attention_probabilities(q, k, scale: float):
+    """The softmax matrix P = softmax(scale * q k^T) row by row, float64.
+
+    Same definition as ``attention_reference``; materialises P, so it is meant
+    for small sizes (invariant checks: rows are non-negative and sum to one).
+    """
+    q, k = _f64(q), _f64(k)
+    if q.ndim < 2 or k.shape[:-2] != q.shape[:-2] or k.shape[-1] != q.shape[-1]:
+        raise ValueError("q and k shapes do not match")
+    scores = np.float64(scale) * (q @ np.swapaxes(k, -1, -2))
+    m = scores.max(axis=-1, keepdims=True)
+    e = np.exp(scores - m)
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def attention_online(q, k, v, scale: float, block: int):
+    """The pages' streaming algorithm over K/V blocks, in float64.
+
+    "FlashAttention, simplified", "The trick": starting from m = -inf, l = 0,
+    acc = 0, for each block of ``block`` consecutive keys (the last one may be
+    shorter):
+        S     = scale * q k_blk^T
+        m_new = max(m, rowmax(S))
+        alpha = exp(m - m_new)
+        l     = alpha * l + rowsum(exp(S - m_new))
+        acc   = alpha * acc + exp(S - m_new) v_blk
+        m     = m_new
+    and finally O = acc / l.  LSE = m + ln l (the same reading as above).
+    All query rows are carried together: query rows never interact.
+    Returns (O, LSE) like ``attention_reference``.
+    """
+    if block < 1:
+        raise ValueError("block must be >= 1")
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    _check(q, k, v)
+    lead = q.shape[:-2]
+    nq, nk, dv = q.shape[-2], k.shape[-2], v.shape[-1]
+    if nk == 0 and nq > 0:
+        raise ValueError("softmax over zero keys is undefined")
+    s = np.float64(scale)
+    out = np.empty(lead + (nq, dv), dtype=np.float64)
+    lse = np.empty(lead + (nq,), dtype=np.float64)
+    for idx in np.ndindex(*lead):
+        qh, kh, vh = q[idx], k[idx], v[idx]
+        m = np.full(nq, -np.inf)
+        l = np.zeros(nq)
+        acc = np.zeros((nq, dv))
+        for j0 in range(0, nk, block):
+            j1 = min(nk, j0 + block)
+            scores = s * (qh @ kh[j0:j1].T)
+            m_new = np.maximum(m, scores.max(axis=1))
+            alpha = np.exp(m - m_new)
+            e = np.exp(scores - m_new[:, None])
+            l = alpha * l + e.sum(axis=1)
+            acc = alpha[:, None] * acc + e @ vh[j0:j1]
+            m = m_new
+        out[idx] = acc / l[:, None]
+        lse[idx] = m + np.log(l)
+    return out, lse

@@ -1,0 +1,111 @@
+"""Planted mistakes in copies of the oracle must each fail at least one pin.
+
+This shows the pins are discriminating: a dropped scale, a transposed score
+matrix, a wrong logarithm base, a missing maximum shift, a wrong rescale factor
+or a lost ragged block would not slip through. Everything here runs on the
+CPU; nothing touches the GPU.
+"""
+import numpy as np
+import pytest
+
+from pins import failing_pins
+
+MUTATIONS = [
+    "drop_scale",
+    "scale_twice",
+    "negate_scores",
+    "transpose_scores",
+    "lse_log2",
+    "lse_without_max",
+    "no_max_shift",
+    "softmax_wrong_axis",
+    "no_normalisation",
+    "online_alpha_inverted",
+    "online_no_rescale_acc",
+    "online_no_rescale_sum",
+    "online_drop_ragged_block",
+    "online_stale_max",
+]
+
+
+def _mutant(q, k, v, scale, mutation):
+    """One head-batched attention with a single planted mistake."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    s = float(scale)
+    if mutation.startswith("online_"):
+        return _online_mutant(q, k, v, s, mutation, block=7)
+    if mutation == "drop_scale":
+        s = 1.0
+    if mutation == "scale_twice":
+        s = s * s
+    if mutation == "negate_scores":
+        s = -s
+    kt = np.swapaxes(k, -1, -2)
+    scores = s * (q @ kt)
+    if mutation == "transpose_scores":
+        if scores.shape[-1] != scores.shape[-2]:
+            raise ValueError("shape")
+        scores = np.swapaxes(scores, -1, -2)
+    axis = -2 if mutation == "softmax_wrong_axis" else -1
+    m = scores.max(axis=axis, keepdims=True)
+    e = np.exp(scores) if mutation == "no_max_shift" else np.exp(scores - m)
+    if mutation == "no_max_shift":
+        m = np.zeros_like(m)
+    l = e.sum(axis=axis, keepdims=True)
+    p = e if mutation == "no_normalisation" else e / l
+    o = p @ v
+    if axis == -2:
+        m, l = np.swapaxes(m, -1, -2), np.swapaxes(l, -1, -2)
+    if mutation == "lse_log2":
+        lse = m[..., 0] + np.log2(l[..., 0])
+    elif mutation == "lse_without_max":
+        lse = np.log(l[..., 0])
+    else:
+        lse = m[..., 0] + np.log(l[..., 0])
+    return o, lse
+
+
+def _online_mutant(q, k, v, s, mutation, block):
+    lead = q.shape[:-2]
+    nq, nk, dv = q.shape[-2], k.shape[-2], v.shape[-1]
+    out = np.empty(lead + (nq, dv))
+    lse = np.empty(lead + (nq,))
+    stop = nk - nk % block if mutation == "online_drop_ragged_block" and nk > block else nk
+    for idx in np.ndindex(*lead):
+        m = np.full(nq, -np.inf)
+        l = np.zeros(nq)
+        acc = np.zeros((nq, dv))
+        for j0 in range(0, stop, block):
+            j1 = min(nk, j0 + block)
+            sc = s * (q[idx] @ k[idx][j0:j1].T)
+            if mutation == "online_stale_max":
+                m_new = np.maximum(m, sc[:, 0])  # only looks at the first key
+            else:
+                m_new = np.maximum(m, sc.max(axis=1))
+            if mutation == "online_alpha_inverted":
+                alpha = np.exp(np.where(np.isfinite(m), m_new - m, -np.inf))
+            else:
+                alpha = np.exp(m - m_new)
+            e = np.exp(sc - m_new[:, None])
+            l = (l if mutation == "online_no_rescale_sum" else alpha * l) + e.sum(axis=1)
+            acc = (acc if mutation == "online_no_rescale_acc" else alpha[:, None] * acc) + e @ v[idx][j0:j1]
+            m = m_new
+        out[idx] = acc / l[:, None]
+        lse[idx] = m + np.log(l)
+    return out, lse
+
+
+@pytest.mark.parametrize("mutation", MUTATIONS)
+def test_planted_mistake_is_caught(mutation):
+    bad = failing_pins(lambda q, k, v, s: _mutant(q, k, v, s, mutation))
+    assert bad, f"mutation {mutation} passed every pin"
+
+
+def test_unmutated_copy_passes():
+    """The mutant scaffold itself, with no mutation, passes every pin (so the
+    failures above come from the planted mistakes)."""
+    assert failing_pins(lambda q, k, v, s: _mutant(q, k, v, s, "none")) == []
+    assert failing_pins(lambda q, k, v, s: _online_mutant(
+        np.asarray(q, float), np.asarray(k, float), np.asarray(v, float), float(s), "online_none", 7)) == []

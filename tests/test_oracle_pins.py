@@ -1,0 +1,96 @@
+"""The CPU oracle held to brute force, closed forms, invariants and a library
+routine (no GPU needed)."""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import attention_online, attention_probabilities, attention_reference
+from pins import ALL_PINS, decimal_attention, support_function_bounds
+
+
+@pytest.mark.parametrize("pin", ALL_PINS, ids=lambda p: p.__name__)
+def test_reference_meets_pin(pin):
+    pin(attention_reference)
+
+
+@pytest.mark.parametrize("block", [1, 7, 128])
+@pytest.mark.parametrize("pin", ALL_PINS, ids=lambda p: p.__name__)
+def test_online_meets_pin(pin, block):
+    pin(lambda q, k, v, s: attention_online(q, k, v, s, block))
+
+
+@pytest.mark.parametrize("block", [1, 7, 16, 128, 300, 1000])
+def test_tiling_invariance(block):
+    """The streaming loop over any K/V tiling gives the definition's O to 1e-12
+    ("FlashAttention, simplified", "The trick": the output is the same as
+    standard attention). N = 300 leaves a ragged last block for most sizes."""
+    rng = np.random.default_rng(11)
+    q, k, v = (rng.standard_normal((2, 300, 32)) for _ in range(3))
+    q *= 3.0  # peaky rows: the running maximum moves often
+    o_ref, lse_ref = attention_reference(q, k, v, 1 / math.sqrt(32))
+    o, lse = attention_online(q, k, v, 1 / math.sqrt(32), block)
+    assert np.max(np.abs(o - o_ref)) <= 1e-12
+    assert np.max(np.abs(lse - lse_ref)) <= 1e-12
+
+
+def test_probabilities_rows():
+    """Every softmax row is non-negative and sums to one."""
+    rng = np.random.default_rng(12)
+    q, k = (4.0 * rng.standard_normal((3, 120, 16)) for _ in range(2))
+    p = attention_probabilities(q, k, 0.25)
+    assert p.shape == (3, 120, 120)
+    assert np.all(p >= 0.0)
+    assert np.max(np.abs(p.sum(axis=-1) - 1.0)) <= 1e-14
+
+
+def test_probabilities_match_decimal():
+    rng = np.random.default_rng(13)
+    q, k = (rng.standard_normal((7, 5)) for _ in range(2))
+    p = attention_probabilities(q[None], k[None], 0.9)[0]
+    _, lse_ref = decimal_attention(q, k, np.eye(7), 0.9)
+    # With V = I the decimal output rows are the softmax rows themselves.
+    o_ref, _ = decimal_attention(q, k, np.eye(7), 0.9)
+    assert np.max(np.abs(p - o_ref)) <= 1e-15
+    assert np.all(np.isfinite(lse_ref))
+
+
+def test_row_blocking_does_not_change_result(monkeypatch):
+    """Blocks of complete rows leave the row-wise definition unchanged."""
+    import oracle.attention as oa
+
+    rng = np.random.default_rng(14)
+    q, k, v = (rng.standard_normal((1, 2, 200, 16)) for _ in range(3))
+    o1, l1 = attention_reference(q, k, v, 0.3)
+    monkeypatch.setattr(oa, "_BLOCK_BYTES", 8 * 200 * 3)  # three rows per block
+    o2, l2 = attention_reference(q, k, v, 0.3)
+    # BLAS may block a matmul differently by shape: equal to rounding only.
+    assert np.max(np.abs(o1 - o2)) <= 1e-14 and np.max(np.abs(l1 - l2)) <= 1e-14
+
+
+def test_rows_subset_equal_full():
+    """Oracle rows depend only on their own query row: a sampled subset of query
+    rows gives exactly the rows of the full result."""
+    rng = np.random.default_rng(15)
+    q, k, v = (rng.standard_normal((1, 1, 64, 8)) for _ in range(3))
+    o, lse = attention_reference(q, k, v, 0.5)
+    idx = np.array([0, 5, 63])
+    o_s, lse_s = attention_reference(q[:, :, idx], k, v, 0.5)
+    assert np.allclose(o_s, o[:, :, idx], rtol=0, atol=1e-15)
+    assert np.allclose(lse_s, lse[:, :, idx], rtol=0, atol=1e-15)
+
+
+def test_zero_keys_rejected_and_empty_queries_ok():
+    z = np.zeros((1, 0, 4))
+    with pytest.raises(ValueError):
+        attention_reference(np.zeros((1, 2, 4)), z, z, 1.0)
+    o, lse = attention_reference(z, np.zeros((1, 3, 4)), np.zeros((1, 3, 4)), 1.0)
+    assert o.shape == (1, 0, 4) and lse.shape == (1, 0)
+
+
+def test_support_function_detects_outside_point():
+    v = np.array([[[0.0, 0.0], [1.0, 0.0], [0.0, 1.0]]])
+    inside = np.array([[[0.2, 0.2]]])
+    outside = np.array([[[0.8, 0.8]]])
+    assert support_function_bounds(inside, v) <= 0.0
+    assert support_function_bounds(outside, v) > 0.0
