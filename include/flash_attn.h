@@ -1,0 +1,116 @@
+/*
+ * flash_attn.h -- C interface of libflashattn.so: exact non-causal scaled
+ * dot-product attention on an AMD Instinct MI355X (gfx950).
+ *
+ * The operation (all entry points):
+ *   for every batch b and head h, with S = scale * Q K^T over the N tokens,
+ *     O   = softmax_rows(S) V
+ *     LSE = ln sum_j exp(S_ij)                 (natural log, one per query row)
+ *   This is attention as defined in "FlashAttention" (interactiveprimer),
+ *   intro and "The bottleneck is memory, not multiplication": an N x N score
+ *   matrix, a row softmax, a product with the values. "scale" is the caller's
+ *   factor (the pages say the scores are scaled but fix no value; 1/sqrt(d)
+ *   is the usual choice). LSE is the softmax's per-row normaliser ln(sum);
+ *   it is not on the pages and is returned so partial results can be merged.
+ *
+ * Layout (all entry points):
+ *   q, k, v, o : contiguous [B, H, N, d] of the element type `dtype`, row major,
+ *                d fastest. o has the element type of the inputs.
+ *   lse        : contiguous [B, H, N] float32.
+ *   Every pointer is a DEVICE pointer owned by the caller; the library keeps
+ *   none of them after a call returns. Outputs must not alias inputs.
+ *   Base pointers must be 16-byte aligned.
+ *
+ * Supported: dtype FA_F32, FA_F16, FA_BF16; d in {64, 128}; any N >= 1.
+ * B, H or N equal to 0 is an empty problem: FA_OK, nothing is launched or
+ * written, and pointers are not examined.
+ *
+ * Errors: arguments are validated before any HIP call; on a validation error
+ * nothing is launched and nothing is written. FA_ERR_HIP reports a launch
+ * failure (hipGetLastError after the launch). NaN or Inf inputs are not
+ * screened: they propagate into the outputs.
+ *
+ * Streams: `stream` is a hipStream_t passed as void*; NULL selects the null
+ * stream. Calls are asynchronous on that stream and never synchronise.
+ * The library holds no per-call state, so calls from several host threads
+ * are safe.
+ */
+#ifndef FLASH_ATTN_H
+#define FLASH_ATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { FA_F32 = 0, FA_F16 = 1, FA_BF16 = 2 } fa_dtype;
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_NULL = 1,        /* a required pointer is NULL                      */
+  FA_ERR_SHAPE = 2,       /* a negative size, or a size product overflows   */
+  FA_ERR_UNSUPPORTED = 3, /* unsupported dtype or head size d               */
+  FA_ERR_ALIGN = 4,       /* a base pointer is not 16-byte aligned          */
+  FA_ERR_WORKSPACE = 5,   /* naive path: workspace smaller than one head    */
+  FA_ERR_SCALE = 6,       /* scale is NaN or infinite                       */
+  FA_ERR_HIP = 7          /* the HIP runtime reported an error at launch    */
+} fa_status;
+
+/*
+ * flash_attn_fwd -- the fused, tiled forward pass.
+ *
+ * Method: "FlashAttention, simplified", section "The trick", and
+ * "FlashAttention" (interactiveprimer), "The bottleneck is memory, not
+ * multiplication": one workgroup per (batch, head, tile of query rows) keeps
+ * its query tile on chip, streams K and V tiles through on-chip memory, keeps
+ * a running row maximum and running sum (online softmax), rescales its
+ * accumulator when the maximum grows and divides by the sum once at the end.
+ * The N x N scores never reach device memory; device-memory traffic is
+ * O(N) per head ("What FlashAttention actually buys", "The actual problem").
+ *
+ * Arguments: q, k, v [B,H,N,d] inputs; o [B,H,N,d] output; lse [B,H,N] float32
+ * output, or NULL to skip it; scale finite (any sign; 0 gives the mean of V).
+ * Arithmetic: for FA_F16/FA_BF16, products on the matrix cores with float32
+ * accumulation, softmax statistics in float32, probabilities rounded to the
+ * input type before the product with V, O rounded to nearest even. For
+ * FA_F32 every step is float32.
+ * Results are deterministic: the same inputs give bitwise the same outputs.
+ * Returns an fa_status.
+ */
+int flash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int H, int N, int d, float scale, int dtype, void* stream);
+
+/*
+ * attn_naive_workspace_bytes -- workspace for attn_naive_fwd to process every
+ * head in one pass: B*H*N*N*(4 + e) bytes, e = element size of dtype (S is
+ * held in float32, P in the input type). Any workspace of at least one head,
+ * N*N*(4 + e) bytes, is accepted: heads are then processed in chunks.
+ * Returns 0 for an unsupported dtype, a negative size or on overflow.
+ */
+size_t attn_naive_workspace_bytes(int B, int H, int N, int dtype);
+
+/*
+ * attn_naive_fwd -- standard, materialising attention in three passes, kept
+ * as the traffic comparator ("FlashAttention, simplified", "The problem";
+ * "What FlashAttention actually buys", "The actual problem"):
+ *   pass 1  S = scale * Q K^T            written to the workspace (float32)
+ *   pass 2  P = softmax_rows(S), LSE     S read back, P written (input type)
+ *   pass 3  O = P V                      P read back
+ * Same arguments, layout and result as flash_attn_fwd, plus `workspace`, a
+ * caller-owned device buffer of `workspace_bytes` (16-byte aligned), which is
+ * overwritten. Fails with FA_ERR_WORKSPACE if it holds less than one head.
+ * lse may be NULL.
+ */
+int attn_naive_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int H, int N, int d, float scale, int dtype,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* fa_strerror -- a static, human-readable string for an fa_status value. */
+const char* fa_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLASH_ATTN_H */

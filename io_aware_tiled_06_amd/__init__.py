@@ -1,0 +1,188 @@
+"""MI355X (gfx950) attention forward pass: thin Python binding of libflashattn.so.
+
+The binding only marshals arguments: every step of the computation runs in
+the HIP kernels of ``libflashattn.so`` (built by ``io_aware_tiled_06_amd.build``).
+There is no CPU fallback; without the built library, or with tensors that are
+not on a GPU, calls raise.
+
+    o, lse = flash_attn_fwd(q, k, v)            # q, k, v: [B, H, N, d] on the GPU
+    o, lse = attn_naive_fwd(q, k, v)            # three-pass comparator
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+__all__ = [
+    "FlashAttnError",
+    "flash_attn_fwd",
+    "attn_naive_fwd",
+    "attn_naive_workspace_bytes",
+    "lib",
+    "LIB_PATH",
+    "EXPORTED_SYMBOLS",
+    "DTYPE_CODE",
+    "FA_OK",
+    "FA_ERR_NULL",
+    "FA_ERR_SHAPE",
+    "FA_ERR_UNSUPPORTED",
+    "FA_ERR_ALIGN",
+    "FA_ERR_WORKSPACE",
+    "FA_ERR_SCALE",
+    "FA_ERR_HIP",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libflashattn.so")
+EXPORTED_SYMBOLS = ("flash_attn_fwd", "attn_naive_workspace_bytes", "attn_naive_fwd", "fa_strerror")
+
+# fa_status values (include/flash_attn.h)
+FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED = 0, 1, 2, 3
+FA_ERR_ALIGN, FA_ERR_WORKSPACE, FA_ERR_SCALE, FA_ERR_HIP = 4, 5, 6, 7
+# fa_dtype values
+DTYPE_CODE = {"fp32": 0, "fp16": 1, "bf16": 2}
+
+_lib = None
+
+
+class FlashAttnError(RuntimeError):
+    """A non-zero fa_status returned by the library."""
+
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {strerror(status)} (status {status})")
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libflashattn.so with argument types declared."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is not built; run `python -m io_aware_tiled_06_amd.build` (needs hipcc)")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        L.flash_attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
+        L.flash_attn_fwd.restype = i
+        L.attn_naive_workspace_bytes.argtypes = [i, i, i, i]
+        L.attn_naive_workspace_bytes.restype = sz
+        L.attn_naive_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, sz, vp]
+        L.attn_naive_fwd.restype = i
+        L.fa_strerror.argtypes = [i]
+        L.fa_strerror.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def strerror(status: int) -> str:
+    return lib().fa_strerror(int(status)).decode()
+
+
+def _dtype_code(t) -> int:
+    import torch
+
+    codes = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+    if t.dtype not in codes:
+        raise TypeError(f"unsupported dtype {t.dtype}; expected float32, float16 or bfloat16")
+    return codes[t.dtype]
+
+
+def _check_inputs(q, k, v):
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be on the GPU (got {t.device}); there is no CPU path")
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be [B, H, N, d]")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if not (q.shape == k.shape == v.shape):
+        raise ValueError(f"q, k, v shapes differ: {tuple(q.shape)}, {tuple(k.shape)}, {tuple(v.shape)}")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v dtypes differ")
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k, v are on different devices")
+
+
+def _default_scale(d: int) -> float:
+    import numpy as np
+
+    return float(np.float32(1.0 / math.sqrt(d)))
+
+
+def _outputs(q, out, return_lse):
+    import torch
+
+    B, H, N, _ = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype or out.device != q.device or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor of q's shape, dtype and device")
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if return_lse else None
+    return out, lse
+
+
+def _stream_ptr(q, stream):
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def flash_attn_fwd(q, k, v, scale=None, *, out=None, return_lse=True, stream=None):
+    """Fused tiled attention forward pass on the GPU.
+
+    q, k, v: contiguous [B, H, N, d] tensors (float32, float16 or bfloat16) on
+    one GPU; d in {64, 128}. scale defaults to 1/sqrt(d) rounded to float32.
+    Returns (o, lse): o like q, lse float32 [B, H, N] (None if not requested).
+    The call is asynchronous on ``stream`` (default: the current stream).
+    """
+    import torch
+
+    _check_inputs(q, k, v)
+    B, H, N, d = q.shape
+    s = _default_scale(d) if scale is None else float(scale)
+    o, lse = _outputs(q, out, return_lse)
+    with torch.cuda.device(q.device):
+        st = lib().flash_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                  lse.data_ptr() if lse is not None else None,
+                                  B, H, N, d, s, _dtype_code(q), _stream_ptr(q, stream))
+    if st != FA_OK:
+        raise FlashAttnError(st, "flash_attn_fwd")
+    return o, lse
+
+
+def attn_naive_workspace_bytes(B: int, H: int, N: int, dtype: str) -> int:
+    """Workspace for the three-pass path to process all heads at once."""
+    return int(lib().attn_naive_workspace_bytes(B, H, N, DTYPE_CODE[dtype]))
+
+
+def attn_naive_fwd(q, k, v, scale=None, *, out=None, return_lse=True, workspace=None, stream=None):
+    """Three-pass materialising attention (S and P through device memory).
+
+    Same arguments and results as ``flash_attn_fwd``. ``workspace`` is a
+    uint8 GPU tensor of at least one head's N*N*(4 + element size) bytes; by
+    default one large enough for every head is allocated.
+    """
+    import torch
+
+    _check_inputs(q, k, v)
+    B, H, N, d = q.shape
+    s = _default_scale(d) if scale is None else float(scale)
+    o, lse = _outputs(q, out, return_lse)
+    if workspace is None:
+        nbytes = int(lib().attn_naive_workspace_bytes(B, H, N, _dtype_code(q)))
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    with torch.cuda.device(q.device):
+        st = lib().attn_naive_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                  lse.data_ptr() if lse is not None else None,
+                                  B, H, N, d, s, _dtype_code(q), workspace.data_ptr(), ws_bytes,
+                                  _stream_ptr(q, stream))
+    if st != FA_OK:
+        raise FlashAttnError(st, "attn_naive_fwd")
+    return o, lse

@@ -1,0 +1,112 @@
+"""Build libflashattn.so (gfx950) in-tree with hipcc.
+
+    python -m io_aware_tiled_06_amd.build
+
+Every source is compiled for gfx950 only. The per-kernel register, LDS and
+scratch usage reported by the compiler is written next to the objects
+(``_build/resource_usage.txt``); a kernel that spills to scratch fails the
+build.
+"""
+from __future__ import annotations
+
+import concurrent.futures as cf
+import os
+import re
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD = os.path.join(PKG, "_build")
+LIB_NAME = "libflashattn.so"
+LIB_PATH = os.path.join(PKG, LIB_NAME)
+SOURCES = ["api.hip", "flash_fwd.hip", "naive.hip"]
+ARCH = "gfx950"
+
+HIPCC_FLAGS = [
+    f"--offload-arch={ARCH}",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    # Packed float32 instructions are kept out of generated code on purpose.
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Rpass-analysis=kernel-resource-usage",
+    f"-I{INCLUDE}",
+    f"-I{CSRC}",
+]
+
+
+def _hipcc() -> str:
+    exe = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(exe):
+        raise RuntimeError("hipcc not found: the HIP toolchain is required to build libflashattn.so")
+    return exe
+
+
+def _compile(src: str) -> tuple[str, str]:
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+    cmd = [_hipcc(), *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
+    return obj, r.stderr
+
+
+def parse_resource_usage(report: str) -> dict:
+    """Per-kernel figures from the compiler's kernel-resource-usage remarks."""
+    kernels: dict = {}
+    cur = None
+    for line in report.splitlines():
+        m = re.search(r"remark: Function Name: (\S+)", line)
+        if m:
+            cur = kernels.setdefault(m.group(1), {})
+            continue
+        m = re.search(r"remark:\s+([A-Za-z][A-Za-z /\[\]]*?): (\d+) \[", line)
+        if m and cur is not None:
+            cur[m.group(1).strip()] = int(m.group(2))
+    return kernels
+
+
+def _check_spills(kernels: dict) -> None:
+    # SGPR spills land in VGPR lanes, not memory; only scratch use counts.
+    bad = {k: v for k, v in kernels.items()
+           if v.get("ScratchSize [bytes/lane]", 0) or v.get("VGPRs Spill", 0)}
+    if bad:
+        raise RuntimeError(f"kernels use scratch memory (register spills): {sorted(bad)}")
+
+
+def build(verbose: bool = False) -> str:
+    """Compile all sources and link the shared library; returns its path."""
+    os.makedirs(BUILD, exist_ok=True)
+    with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+        results = list(ex.map(_compile, SOURCES))
+    objs = [o for o, _ in results]
+    report = "\n".join(r for _, r in results)
+    with open(os.path.join(BUILD, "resource_usage.txt"), "w") as f:
+        f.write(report)
+    kernels = parse_resource_usage(report)
+    if not kernels:
+        raise RuntimeError("no kernel-resource-usage remarks found in the compiler output")
+    _check_spills(kernels)
+    with open(os.path.join(BUILD, "resource_summary.txt"), "w") as f:
+        for name, v in sorted(kernels.items()):
+            f.write(f"{name} VGPRs={v.get('VGPRs')} AGPRs={v.get('AGPRs')} "
+                    f"scratch={v.get('ScratchSize [bytes/lane]')} occupancy={v.get('Occupancy [waves/SIMD]')} "
+                    f"LDS={v.get('LDS Size [bytes/block]')}\n")
+    tmp = LIB_PATH + ".tmp"
+    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stderr}")
+    os.replace(tmp, LIB_PATH)
+    if verbose:
+        print(f"built {LIB_PATH}")
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    build(verbose=True)
+    sys.exit(0)

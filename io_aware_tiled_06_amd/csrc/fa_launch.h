@@ -1,0 +1,42 @@
+// fa_launch.h -- host-side launchers behind the C interface. Arguments reach
+// these only after validation (see api.hip); they launch and return the HIP
+// status of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fa {
+
+enum ElemType { kF32 = 0, kF16 = 1, kBF16 = 2 };
+
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;  // may be null
+  int B, H, N, d;
+  float scale;
+  int dtype;
+  hipStream_t stream;
+};
+
+inline int elem_bytes(int dtype) { return dtype == kF32 ? 4 : 2; }
+
+// Query rows per workgroup of the fused kernel for (dtype, d).
+int flash_rows_per_block(int dtype, int d);
+
+// Fused tiled forward pass over all B*H heads (one launch).
+hipError_t launch_flash(const AttnArgs& a);
+
+// Largest number of heads one launch of the three-pass path may cover
+// (grid-size limit); 0 means N is too large for that path.
+int64_t naive_max_heads_per_launch(int N, int d, int dtype);
+
+// Three-pass materialising forward pass; heads are processed in chunks that
+// fit `ws_bytes` (at least one head).
+hipError_t launch_naive(const AttnArgs& a, void* ws, size_t ws_bytes);
+
+}  // namespace fa

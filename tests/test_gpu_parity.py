@@ -1,0 +1,232 @@
+"""HIP path against the float64 CPU oracle on the same seeded inputs.
+
+Tolerances (both entry points): float32 inputs max|dO| <= 1e-5 at the usual
+scale 1/sqrt(d); float16 and bfloat16 inputs max|dO| <= 2e-2 and relative RMS
+||dO||/||O|| <= 1e-2 over the compared rows; every dtype max|dLSE| <= 1e-3
+(absolute, natural log). float32 rounding of the scores grows with their
+magnitude, so for another scale s the float32 bound is 1e-5 * max(1, |s|*sqrt(d))
+(at s = 4, d = 64 torch's own float32 CPU attention is 3.5e-5 off).
+The long-context workload is compared on sampled query rows (each row of the
+oracle depends only on that row), at full size and in the launch the
+benchmark times.
+"""
+import math
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import io_aware_tiled_06_amd as fa  # noqa: E402
+from io_aware_tiled_06_amd.workloads import WORKLOADS, Workload, make_inputs, sample_rows  # noqa: E402
+from oracle import attention_reference  # noqa: E402
+from pins import support_function_bounds  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+TORCH_DT = {"fp32": torch.float32, "fp16": torch.float16, "bf16": torch.bfloat16}
+MAX_ABS = {"fp32": 1e-5, "fp16": 2e-2, "bf16": 2e-2}
+REL_RMS = 1e-2
+LSE_TOL = 1e-3
+
+
+def dev(x, dtype):
+    return torch.from_numpy(np.ascontiguousarray(x)).to(TORCH_DT[dtype]).cuda()
+
+
+def host(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def max_abs_tol(dtype, scale=None, d=None):
+    """max|dO| bound; float32 scales with |scale|*sqrt(d) beyond the usual scale."""
+    tol = MAX_ABS[dtype]
+    if dtype == "fp32" and scale is not None:
+        tol *= max(1.0, abs(scale) * math.sqrt(d))
+    return tol
+
+
+def assert_close(o, lse, o_ref, lse_ref, dtype, what="", tol=None):
+    d = o - o_ref
+    max_abs = float(np.max(np.abs(d))) if d.size else 0.0
+    tol = MAX_ABS[dtype] if tol is None else tol
+    assert np.all(np.isfinite(o)), f"{what}: non-finite O"
+    assert max_abs <= tol, f"{what}: max|dO| = {max_abs:.3e} > {tol:.1e}"
+    if dtype != "fp32" and d.size:
+        rel = float(np.linalg.norm(d) / max(np.linalg.norm(o_ref), 1e-300))
+        assert rel <= REL_RMS, f"{what}: relative RMS = {rel:.3e}"
+    if lse is not None:
+        dl = float(np.max(np.abs(lse - lse_ref))) if lse.size else 0.0
+        assert dl <= LSE_TOL, f"{what}: max|dLSE| = {dl:.3e}"
+
+
+def run(entry, q, k, v, dtype, scale, **kw):
+    tq, tk, tv = dev(q, dtype), dev(k, dtype), dev(v, dtype)
+    o, lse = entry(tq, tk, tv, scale, **kw)
+    torch.cuda.synchronize()
+    return host(o), (lse.cpu().numpy().astype(np.float64) if lse is not None else None)
+
+
+ENTRIES = {"flash": fa.flash_attn_fwd, "naive": fa.attn_naive_fwd}
+
+
+# -- the named workloads -------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["n256_d64_fp32", "n4096_d128_bf16", "n10000_d128_fp16", "b32_n512_d64_bf16"])
+@pytest.mark.parametrize("entry", ["flash", "naive"])
+def test_workload_full(name, entry):
+    w = WORKLOADS[name]
+    print(f"[parity] {entry} {name}", flush=True)
+    q, k, v = make_inputs(w)
+    o, lse = run(ENTRIES[entry], q, k, v, w.dtype, w.scale)
+    o_ref, lse_ref = attention_reference(q, k, v, w.scale)
+    assert_close(o, lse, o_ref, lse_ref, w.dtype, f"{entry} {name}")
+
+
+@pytest.fixture(scope="module")
+def long_context():
+    w = WORKLOADS["n32768_d128_bf16"]
+    q, k, v = make_inputs(w)
+    tq, tk, tv = dev(q, w.dtype), dev(k, w.dtype), dev(v, w.dtype)
+    return w, (q, k, v), (tq, tk, tv)
+
+
+def test_long_context_sampled_rows(long_context):
+    """Full-size 32K workload, the benchmark's launch; 96 sampled rows per head."""
+    w, (q, k, v), (tq, tk, tv) = long_context
+    print("[parity] flash n32768_d128_bf16 sampled rows", flush=True)
+    o, lse = fa.flash_attn_fwd(tq, tk, tv, w.scale)
+    torch.cuda.synchronize()
+    rows = sample_rows(w.N, 96)
+    o_s = o[:, :, rows].float().cpu().numpy().astype(np.float64)
+    lse_s = lse[:, :, rows].cpu().numpy().astype(np.float64)
+    o_ref, lse_ref = attention_reference(q[:, :, rows], k, v, w.scale)
+    assert_close(o_s, lse_s, o_ref, lse_ref, w.dtype, "n32768 sampled")
+    # every row (not only the sampled ones) lies in the convex hull of V's rows
+    for h in range(w.H):
+        excess = support_function_bounds(o[0, h].float().cpu().numpy(), v[0, h])
+        assert excess <= 2e-2, (h, excess)
+
+
+def test_long_context_naive_chunked(long_context):
+    """Three-pass path at 32K with a workspace of 3 heads (chunks of 3,3,...,1)."""
+    w, (q, k, v), (tq, tk, tv) = long_context
+    print("[parity] naive n32768_d128_bf16 sampled rows, chunked", flush=True)
+    per_head = w.N * w.N * 6
+    ws = torch.empty(3 * per_head, dtype=torch.uint8, device="cuda")
+    o, lse = fa.attn_naive_fwd(tq, tk, tv, w.scale, workspace=ws)
+    torch.cuda.synchronize()
+    del ws
+    rows = sample_rows(w.N, 32)
+    o_s = o[:, :, rows].float().cpu().numpy().astype(np.float64)
+    lse_s = lse[:, :, rows].cpu().numpy().astype(np.float64)
+    o_ref, lse_ref = attention_reference(q[:, :, rows], k, v, w.scale)
+    assert_close(o_s, lse_s, o_ref, lse_ref, w.dtype, "naive n32768 sampled")
+
+
+# -- ragged and small shapes ------------------------------------------------------
+
+EDGE_N = [1, 2, 17, 127, 128, 129, 255, 257]
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "fp16", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("n", EDGE_N)
+@pytest.mark.parametrize("entry", ["flash", "naive"])
+def test_edge_shapes(entry, n, d, dtype):
+    w = Workload("edge", 2, 3, n, d, dtype, 1000 + n + d)
+    q, k, v = make_inputs(w)
+    o, lse = run(ENTRIES[entry], q, k, v, dtype, w.scale)
+    o_ref, lse_ref = attention_reference(q, k, v, w.scale)
+    assert_close(o, lse, o_ref, lse_ref, dtype, f"{entry} n={n} d={d} {dtype}")
+
+
+@pytest.mark.parametrize("n,d,dtype", [(1000, 128, "bf16"), (3000, 64, "bf16"), (777, 128, "fp16"),
+                                       (2049, 64, "fp16"), (700, 128, "fp32"), (333, 64, "fp32")])
+@pytest.mark.parametrize("entry", ["flash", "naive"])
+def test_multi_tile_ragged(entry, n, d, dtype):
+    w = Workload("ragged", 1, 2, n, d, dtype, 77 + n, 2.0)
+    q, k, v = make_inputs(w)
+    o, lse = run(ENTRIES[entry], q, k, v, dtype, w.scale)
+    o_ref, lse_ref = attention_reference(q, k, v, w.scale)
+    assert_close(o, lse, o_ref, lse_ref, dtype, f"{entry} n={n} d={d} {dtype}")
+
+
+# -- special cases ---------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16", "fp16"])
+@pytest.mark.parametrize("entry", ["flash", "naive"])
+def test_zero_scale_gives_mean(entry, dtype):
+    w = Workload("zero", 1, 2, 300, 128, dtype, 5)
+    q, k, v = make_inputs(w)
+    o, lse = run(ENTRIES[entry], q, k, v, dtype, 0.0)
+    mean = v.astype(np.float64).mean(axis=2, keepdims=True)
+    assert_close(o, lse, np.broadcast_to(mean, o.shape), np.full(lse.shape, math.log(300)), dtype, "scale=0")
+
+
+@pytest.mark.parametrize("scale", [-0.09, 0.6, 4.0])
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("entry", ["flash", "naive"])
+def test_scale_values(entry, scale, dtype):
+    """Negative, large and very large (near one-hot rows) scales."""
+    w = Workload("scales", 1, 2, 389, 64, dtype, 6)
+    q, k, v = make_inputs(w)
+    o, lse = run(ENTRIES[entry], q, k, v, dtype, scale)
+    o_ref, lse_ref = attention_reference(q, k, v, scale)
+    assert_close(o, lse, o_ref, lse_ref, dtype, f"scale={scale}", tol=max_abs_tol(dtype, scale, w.d))
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_constant_values(dtype):
+    w = Workload("const", 1, 1, 500, 128, dtype, 7, 3.0)
+    q, k, v = make_inputs(w)
+    v[:] = v[:, :, :1, :]
+    o, _ = run(fa.flash_attn_fwd, q, k, v, dtype, w.scale)
+    assert np.max(np.abs(o - v[:, :, :1, :])) <= MAX_ABS[dtype]
+
+
+def test_deterministic():
+    w = WORKLOADS["n10000_d128_fp16"].with_(H=2)
+    q, k, v = make_inputs(w)
+    tq, tk, tv = dev(q, w.dtype), dev(k, w.dtype), dev(v, w.dtype)
+    o1, l1 = fa.flash_attn_fwd(tq, tk, tv)
+    o2, l2 = fa.flash_attn_fwd(tq, tk, tv)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_without_lse_and_with_out_tensor():
+    w = Workload("nolse", 2, 2, 200, 128, "bf16", 8)
+    q, k, v = make_inputs(w)
+    tq, tk, tv = dev(q, w.dtype), dev(k, w.dtype), dev(v, w.dtype)
+    ref, _ = fa.flash_attn_fwd(tq, tk, tv)
+    out = torch.empty_like(tq)
+    o, lse = fa.flash_attn_fwd(tq, tk, tv, out=out, return_lse=False)
+    torch.cuda.synchronize()
+    assert lse is None and o.data_ptr() == out.data_ptr() and torch.equal(o, ref)
+
+
+def test_side_stream():
+    w = Workload("stream", 1, 4, 640, 64, "bf16", 9)
+    q, k, v = make_inputs(w)
+    tq, tk, tv = dev(q, w.dtype), dev(k, w.dtype), dev(v, w.dtype)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        o, lse = fa.flash_attn_fwd(tq, tk, tv)
+    s.synchronize()
+    o_ref, lse_ref = attention_reference(q, k, v, w.scale)
+    assert_close(host(o), lse.cpu().numpy(), o_ref, lse_ref, "bf16", "side stream")
+
+
+def test_empty_batch():
+    x = torch.empty((0, 2, 16, 64), dtype=torch.bfloat16, device="cuda")
+    o, lse = fa.flash_attn_fwd(x, x, x)
+    assert o.shape == x.shape and lse.shape == (0, 2, 16)
+
+
+def test_unsupported_head_size_raises():
+    x = torch.zeros((1, 1, 16, 96), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(fa.FlashAttnError) as e:
+        fa.flash_attn_fwd(x, x, x)
+    assert e.value.status == fa.FA_ERR_UNSUPPORTED
