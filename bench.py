@@ -15,7 +15,7 @@ drawn with sigma 3). Prints one JSON line:
              `traffic` is the measured HBM bytes per launch from the committed
              rocprofv3 counter summary when it matches the current kernel source
   cpu_baseline  the float64 CPU oracle timed on this host on a bounded sample of
-             the same workload (whole query rows of one head)
+             the same workload (whole query rows, about 15 s of work)
 """
 from __future__ import annotations
 
@@ -60,7 +60,8 @@ def measured_traffic(workload: str, entry: str):
 
 
 def cpu_baseline(w, q, k, v, target_s: float = 15.0):
-    """Time the float64 oracle on whole query rows of head 0 of the workload."""
+    """Time the float64 oracle for about target_s seconds on whole query rows of
+    the workload (head by head)."""
     import numpy as np
 
     from oracle import attention_reference
@@ -74,23 +75,47 @@ def cpu_baseline(w, q, k, v, target_s: float = 15.0):
         pass
     if threads is None:
         threads = len(os.sched_getaffinity(0))
-    qh, kh, vh = q[0, 0], k[0, 0], v[0, 0]
-    rows = min(w.N, 512)
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    rows0 = min(w.N, 512)
     t0 = time.perf_counter()
-    attention_reference(qh[None, :rows], kh[None], vh[None], w.scale)
+    attention_reference(q[0, 0][None, :rows0], k[0, 0][None], v[0, 0][None], w.scale)
     t_probe = time.perf_counter() - t0
-    rows = int(min(w.N, max(rows, rows * target_s / max(t_probe, 1e-6))))
+    # whole heads first, then a row prefix of the next one, for ~target_s seconds
+    want = int(rows0 * target_s / max(t_probe, 1e-6))
+    n_heads = min(len(heads), want // w.N)
+    rows_last = 0 if n_heads == len(heads) else max(0, min(w.N, want - n_heads * w.N))
+    if n_heads == 0:
+        rows_last = max(rows0, rows_last)
     t0 = time.perf_counter()
-    attention_reference(qh[None, :rows], kh[None], vh[None], w.scale)
+    for b, h in heads[:n_heads]:
+        attention_reference(q[b, h][None], k[b, h][None], v[b, h][None], w.scale)
+    if rows_last:
+        b, h = heads[n_heads]
+        attention_reference(q[b, h][None, :rows_last], k[b, h][None], v[b, h][None], w.scale)
     t = time.perf_counter() - t0
+    rows = n_heads * w.N + rows_last
     flops = 4.0 * rows * w.N * w.d
     return {
         "value": round(flops / t / 1e12, 6),
         "unit": "TFLOP/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": f"{rows} of {w.N} query rows of head 0 against all {w.N} keys, float64 numpy; {t:.2f} s",
+        "sample": (f"{n_heads} whole head(s) + {rows_last} query rows of the next, each row against all "
+                   f"{w.N} keys ({rows} rows of {w.B * w.H * w.N}), float64 numpy; {t:.2f} s"),
     }
+
+
+def copy_calibration(nbytes: int, reps: int) -> None:
+    """A plain device-to-device copy of `nbytes` (torch's copy kernel), to scale
+    the FETCH_SIZE / WRITE_SIZE counters: it reads and writes exactly nbytes."""
+    import torch
+
+    x = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0").fill_(1)
+    y = torch.empty_like(x)
+    for _ in range(reps):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps}), flush=True)
 
 
 def main() -> int:
@@ -101,7 +126,12 @@ def main() -> int:
     ap.add_argument("--workload", default="n32768_d128_bf16")
     ap.add_argument("--entry", choices=["flash", "naive"], default="flash")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES (counter calibration) and exit")
     args = ap.parse_args()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration, 3)
+        return 0
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path",
               file=sys.stderr)

@@ -94,7 +94,7 @@ __device__ __forceinline__ u32x4 ld_global16(const void* p) {
 // Row staging: ROWS rows of ROW_BYTES bytes copied from global memory into
 // LDS at a padded pitch of PITCH bytes. Thread item i covers 16-byte chunk
 // (row i / (ROW_BYTES/16), chunk i % (ROW_BYTES/16)), so consecutive lanes
-// read consecutive bytes of a row. Rows at or past `n_valid` read as zero.
+// read consecutive bytes of a row.
 // K tiles (any element type) and float32 V tiles use this.
 template <int ROWS, int ROW_BYTES, int PITCH, int NT>
 struct RowStage {
@@ -107,15 +107,16 @@ struct RowStage {
   static constexpr int kBytes = ROWS * PITCH;
   u32x4 r[kPer];
 
-  // base: first byte of row 0 of the head; rows are ROW_BYTES apart.
+  // base: first byte of row 0 of the head; rows are ROW_BYTES apart. Rows at
+  // or past n_valid re-read row n_valid - 1: always in bounds, never branched
+  // on; the scores of those keys are masked and their probabilities are 0.
   __device__ __forceinline__ void load(const char* base, int row0, int n_valid, int tid) {
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int item = tid + i * NT;
       const int row = item / kRowChunks, ch = item % kRowChunks;
-      const int key = row0 + row;
-      r[i] = (key < n_valid) ? ld_global16(base + (int64_t)key * ROW_BYTES + ch * 16)
-                             : u32x4{0, 0, 0, 0};
+      const int key = min(row0 + row, n_valid - 1);
+      r[i] = ld_global16(base + (int64_t)key * ROW_BYTES + ch * 16);
     }
   }
   __device__ __forceinline__ void store(char* lds, int tid) const {
@@ -152,16 +153,18 @@ struct VStage {
   static constexpr int kBytes = D * kPitch;
   u32x4 r[kPer][4];
 
+  // Keys at or past n_valid re-read key n_valid - 1 (in bounds, no branch);
+  // their probabilities are 0.
   __device__ __forceinline__ void load(const uint16_t* base, int row0, int n_valid, int tid) {
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int item = tid + i * NT;
+      if (kItems % NT != 0 && item >= kItems) continue;
       const int kg = item % (BC / 4), dg = item / (BC / 4);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int key = row0 + kg * 4 + j;
-        const bool ok = (kItems % NT == 0 || item < kItems) && key < n_valid;
-        r[i][j] = ok ? ld_global16(base + (int64_t)key * D + dg * 8) : u32x4{0, 0, 0, 0};
+        const int key = min(row0 + kg * 4 + j, n_valid - 1);
+        r[i][j] = ld_global16(base + (int64_t)key * D + dg * 8);
       }
     }
   }

@@ -28,6 +28,8 @@
 //    range of every element type). The result is the same in exact
 //    arithmetic because numerator and denominator share the same m.
 //  * Workgroup ids are remapped so that each XCD works on contiguous heads.
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_launch.h"
 
@@ -145,7 +147,10 @@ void flash_fwd_half(FwdParams p) {
   vs.store(smem + KS::kBytes, tid);
   __syncthreads();
 
-  for (int j = 0; j < n_tiles; ++j) {
+  // One K/V tile: scores, online-softmax update, P V. Only the last tile can
+  // hold keys past N; MASK is true for that one alone.
+  auto step = [&](int j, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     const char* kbuf = smem + (j & 1) * kStage;
     const char* vbuf = kbuf + KS::kBytes;
     const bool more = j + 1 < n_tiles;
@@ -165,8 +170,7 @@ void flash_fwd_half(FwdParams p) {
         s[kb] = Mfma<E>::run(KS::read16(kbuf, kb * 32 + l32, (kk * 16 + g * 8) * 2), qf[kk], s[kb]);
 
     const int key0 = j * BC;
-    const bool ragged = key0 + BC > N;
-    if (ragged) hide_tail(s, key0, N, g, c >= 0.f ? -INFINITY : INFINITY);
+    if constexpr (MASK) hide_tail(s, key0, N, g, c >= 0.f ? -INFINITY : INFINITY);
 
     float alpha;
     if (update_max(row_max_scaled(s, c), m_run, l_run, alpha)) {
@@ -188,7 +192,8 @@ void flash_fwd_half(FwdParams p) {
           const int r = h * 8 + 2 * w;
           float p0 = exp2_fast(fmaf(s[kb][r], c, neg_m));
           float p1 = exp2_fast(fmaf(s[kb][r + 1], c, neg_m));
-          if (ragged) {
+          if constexpr (MASK) {
+            // explicit zero: with c == 0 a hidden score would give 0 * inf
             if (key0 + score_key(kb, r, g) >= N) p0 = 0.f;
             if (key0 + score_key(kb, r + 1, g) >= N) p1 = 0.f;
           }
@@ -212,7 +217,10 @@ void flash_fwd_half(FwdParams p) {
       vs.store(nbuf + KS::kBytes, tid);
     }
     __syncthreads();
-  }
+  };
+  const int n_full = N / BC;
+  for (int j = 0; j < n_full; ++j) step(j, std::false_type{});
+  if (n_full < n_tiles) step(n_full, std::true_type{});
 
   // Epilogue: one division per row ("rescale once at the end"), O rounded to
   // nearest even; LSE = ln(2^m * l) = (m + log2 l) * ln 2.
@@ -280,7 +288,8 @@ __global__ __launch_bounds__(NW * 64) void flash_fwd_f32(FwdParams p) {
   vs.store(smem + KS::kBytes, tid);
   __syncthreads();
 
-  for (int j = 0; j < n_tiles; ++j) {
+  auto step = [&](int j, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     const char* kbuf = smem + (j & 1) * kStage;
     const char* vbuf = kbuf + KS::kBytes;
     const bool more = j + 1 < n_tiles;
@@ -298,8 +307,7 @@ __global__ __launch_bounds__(NW * 64) void flash_fwd_f32(FwdParams p) {
     }
 
     const int key0 = j * BC;
-    const bool ragged = key0 + BC > N;
-    if (ragged) hide_tail(s, key0, N, g, c >= 0.f ? -INFINITY : INFINITY);
+    if constexpr (MASK) hide_tail(s, key0, N, g, c >= 0.f ? -INFINITY : INFINITY);
 
     float alpha;
     if (update_max(row_max_scaled(s, c), m_run, l_run, alpha)) {
@@ -312,7 +320,9 @@ __global__ __launch_bounds__(NW * 64) void flash_fwd_f32(FwdParams p) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       float pv = exp2_fast(fmaf(s[0][r], c, -m_run));
-      if (ragged && key0 + score_key(0, r, g) >= N) pv = 0.f;
+      if constexpr (MASK) {
+        if (key0 + score_key(0, r, g) >= N) pv = 0.f;
+      }
       pr[r] = pv;
       lsum += pv;
     }
@@ -333,7 +343,10 @@ __global__ __launch_bounds__(NW * 64) void flash_fwd_f32(FwdParams p) {
       vs.store(nbuf + KS::kBytes, tid);
     }
     __syncthreads();
-  }
+  };
+  const int n_full = N / BC;
+  for (int j = 0; j < n_full; ++j) step(j, std::false_type{});
+  if (n_full < n_tiles) step(n_full, std::true_type{});
 
   const float l_tot = pair_sum(l_run);
   const float inv = 1.f / l_tot;
