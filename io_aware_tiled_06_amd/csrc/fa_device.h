@@ -16,6 +16,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 // Storage tags for the two half-precision element types.
 struct BF16 {};
@@ -41,6 +42,11 @@ template <> struct Mfma<BF16> {
     bf16x2 v = {(__bf16)x, (__bf16)y};
     return __builtin_bit_cast(uint32_t, v);
   }
+  // acc + lo + hi of a packed pair (v_dot2 against (1, 1); exact products)
+  static __device__ __forceinline__ float sum2(uint32_t pair, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair), __builtin_bit_cast(bf16x2, 0x3f803f80u),
+                                           acc, false);
+  }
 };
 template <> struct Mfma<F16> {
   static __device__ __forceinline__ f32x16 run(u32x4 a, u32x4 b, f32x16 c) {
@@ -50,6 +56,9 @@ template <> struct Mfma<F16> {
   static __device__ __forceinline__ uint32_t pack2(float x, float y) {
     f16x2 v = {(_Float16)x, (_Float16)y};
     return __builtin_bit_cast(uint32_t, v);
+  }
+  static __device__ __forceinline__ float sum2(uint32_t pair, float acc) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pair), __builtin_bit_cast(f16x2, 0x3c003c00u), acc, false);
   }
 };
 
@@ -87,9 +96,101 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblk) {
   return xcd * per + (xcd < rem ? xcd : rem) + idx;
 }
 
+// Wait until every vector-memory load issued so far has returned
+// (s_waitcnt vmcnt(0); the expcnt and lgkmcnt fields are left at their
+// maxima, i.e. not waited on). Issued once the loads that a loop reads but
+// never reissues (the query tile) are in flight: the compiler then knows they
+// are complete inside the loop and does not make its first products wait on
+// the loads of the next K/V tile, which come later in the same in-order count.
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+
 __device__ __forceinline__ u32x4 ld_global16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
+
+// ---------------------------------------------------------------------------
+// Direct global -> LDS copies and transposing LDS reads (gfx950).
+// ---------------------------------------------------------------------------
+
+// Raw buffer resource over `bytes` bytes from `base` (stride 0, untyped 32-bit
+// data format, the gfx9 descriptor word 3 = 0x00020000); the hardware returns
+// zero for offsets at or past `bytes`. Four scalar registers.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4 buffer_rsrc(const void* base, int bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const i32x4 r = {(int)(uint32_t)a, (int)((a >> 32) & 0xffffu), bytes, 0x00020000};
+  return r;
+}
+
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)p);
+}
+
+// One 16-byte load per lane from `rsrc` at byte `voff`, written straight into
+// LDS (buffer_load_dwordx4 ... lds): lane i fills LDS bytes
+// [lds + 16 i, lds + 16 i + 16); `lds` is wave-uniform and goes through M0,
+// which is restored afterwards. Completion is counted by vmcnt.
+// Issued as inline assembly on purpose: the compiler then does not know that
+// this load writes LDS, and does not put a full vmcnt wait in front of every
+// later transposing LDS read (it cannot tell them apart from the copy's
+// destination). Every LDS read of copied data is ordered by hand instead: an
+// explicit vmcnt wait (vm_wait) and a workgroup barrier, never by the compiler.
+__device__ __forceinline__ void load_lds16(i32x4 rsrc, uint32_t lds, uint32_t voff) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(voff), "s"(rsrc)
+      : "memory");
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding
+// (they complete in issue order). Inline assembly, so that it stays exactly
+// where it is written; the "memory" clobber keeps memory accesses on their side.
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+// Transposing 8-byte LDS read of 16-bit data (ds_read_b64_tr_b16). Within
+// each group of 16 lanes, source lane s reads four consecutive elements
+// E[s][0..3] at its own address; lane i of the group receives
+// E[4k + i/4][i % 4] for k = 0..3. With source lane s pointing at row
+// (row0 + s/4), columns (col0 + 4 (s%4)) .. +3 of a row-major matrix, lane i
+// therefore receives column col0 + i of rows row0 .. row0 + 3.
+__device__ __forceinline__ u32x2 lds_read_tr16(const char* lds) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)const_cast<char*>(lds));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// 16-byte chunk placement of the K and V tiles in LDS. A tile row r of RB =
+// 2 D bytes is kept at r * RB; its chunk c sits in slot c ^ k(r) (K) or
+// c ^ v(r) (V). The XOR keeps every read of the attention loop free of bank
+// conflicts on 32 or 64 four-byte banks:
+//  * K (16-byte reads): 16 consecutive rows, one chunk -> 16 distinct slots
+//    (d = 128), or 16 distinct (row parity, slot) pairs (d = 64);
+//  * V (transposing 8-byte reads): 4 consecutive rows x 4 consecutive chunks
+//    -> 16 distinct slots (d = 128) / (row parity, slot) pairs (d = 64), and
+//    any 16 lanes of it -> 8 distinct slots modulo 8.
+template <int D> struct TileSwizzle;
+template <> struct TileSwizzle<128> {
+  static __device__ __forceinline__ int k(int r) { return r & 15; }
+  static __device__ __forceinline__ int v(int r) {
+    const int t = r & 3;
+    return 4 * t + 2 * (t >> 1);
+  }
+};
+template <> struct TileSwizzle<64> {
+  static __device__ __forceinline__ int k(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+  static __device__ __forceinline__ int v(int r) { return 2 * (r & 3); }
+};
 
 // Row staging: ROWS rows of ROW_BYTES bytes copied from global memory into
 // LDS at a padded pitch of PITCH bytes. Thread item i covers 16-byte chunk

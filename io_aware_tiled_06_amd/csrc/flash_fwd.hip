@@ -103,141 +103,285 @@ __device__ __forceinline__ bool update_max(float m_tile, float& m_run, float& l_
 
 // ---------------------------------------------------------------------------
 // Half-precision inputs (bf16 / fp16): matrix cores, float32 accumulation.
+//
+// A wave owns QB blocks of 32 query rows. QB = 1 is used: two waves share
+// each SIMD and cover each other's LDS and barrier waits. (QB = 2 halves the
+// LDS reads per flop, since every K or V operand then feeds two products, but
+// needs 448 registers per lane, hence one wave per SIMD; measured slower on
+// MI355X.) Key tiles of BC = 32. K and
+// V tiles are copied from global memory straight into LDS (16 bytes per lane,
+// no register staging) with the chunk placement of TileSwizzle<D>, into a
+// ring of NBUF = 4 buffers each, three tiles ahead of use. The loop is
+// software pipelined: while the matrix cores form the scores of tile j+1, the
+// vector ALUs turn the scores of tile j into probabilities; while the cores
+// add P_j V_j into the accumulator, the vector ALUs find the row maxima of
+// tile j+1. One barrier per tile publishes the tiles two steps ahead and
+// frees the buffers the next copies overwrite.
 // ---------------------------------------------------------------------------
-template <class E, int D, int BC, int NW>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
+template <class E, int D, int NW, int QB>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(QB == 1 ? 2 : 1)))
 void flash_fwd_half(FwdParams p) {
-  constexpr int NT = NW * 64, BR = NW * 32;
-  constexpr int NS = BC / 32;  // 32-key blocks per tile
-  using KS = RowStage<BC, D * 2, D * 2 + 16, NT>;
-  using VS = VStage<D, BC, NT>;
-  constexpr int kStage = KS::kBytes + VS::kBytes;
-  __shared__ __attribute__((aligned(16))) char smem[2 * kStage];
+  constexpr int BR = NW * 32 * QB;
+  constexpr int BC = 32;
+  constexpr int NBUF = 4;
+  constexpr int RB = D * 2;   // bytes per K / V row
+  constexpr int KK = D / 16;  // contraction steps of the score product
+  constexpr int DB = D / 32;  // 32-feature blocks of the output
+  constexpr int kTile = BC * RB;
+  constexpr int kPer = kTile / 1024 / NW;  // 1 KB direct copies per wave per tile
+  static_assert(kTile % (1024 * NW) == 0, "a tile must split into 1 KB copies evenly over the waves");
+  using Swz = TileSwizzle<D>;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * NBUF * kTile];  // K ring, V ring
+  auto kbuf = [&](int b) { return smem + b * kTile; };
+  auto vbuf = [&](int b) { return smem + (NBUF + b) * kTile; };
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, g = lane >> 5;
   const int blk = xcd_remap(blockIdx.x, p.n_blocks);
   const int bh = blk / p.n_qtiles, qt = blk % p.n_qtiles;
   const int N = p.n;
-  const int64_t head = (int64_t)bh * N * D * 2;  // bytes
+  const int64_t head = (int64_t)bh * N * RB;  // bytes
   const char* Q = p.q + head;
   const char* K = p.k + head;
   const char* V = p.v + head;
   const float c = p.c;
 
-  // This lane's query row; rows past the end load row N-1 and are not stored.
-  const int q_row = qt * BR + wave * 32 + l32;
-  const int q_ld = q_row < N ? q_row : N - 1;
-  u32x4 qf[D / 16];
+  // Direct-copy sources. Copy t of this wave fills LDS bytes
+  // [(wave*kPer + t) KB, +1 KB) of a tile; this lane's 16 bytes are row cp_row[t],
+  // slot (pos % RB)/16, which holds chunk slot ^ swizzle(row) of that row.
+  int cp_row[kPer];
+  uint32_t cp_k[kPer], cp_v[kPer];
 #pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk)
-    qf[kk] = ld_global16(Q + ((int64_t)q_ld * D + kk * 16 + g * 8) * 2);
+  for (int t = 0; t < kPer; ++t) {
+    const int pos = (wave * kPer + t) * 1024 + lane * 16;
+    const int r = pos / RB, slot = (pos % RB) / 16;
+    cp_row[t] = r;
+    cp_k[t] = (slot ^ Swz::k(r)) * 16;
+    cp_v[t] = (slot ^ Swz::v(r)) * 16;
+  }
+  // Copy tile `tile` of a head's K or V into `dst`. Rows at or past N (the
+  // ragged last tile only) re-read row N-1: in bounds, never used.
+  auto copy_tile = [&](const char* src, int tile, char* dst, const uint32_t(&col)[kPer]) {
+    const int row0 = tile * BC;
+    const i32x4 rs = buffer_rsrc(src + (int64_t)row0 * RB, kTile);
+    const uint32_t l0 = lds_addr(dst) + wave * kPer * 1024;
+    const int last = N - 1 - row0;
+    if (last >= BC - 1) {
+#pragma unroll
+      for (int t = 0; t < kPer; ++t) load_lds16(rs, l0 + t * 1024, cp_row[t] * RB + col[t]);
+    } else {
+#pragma unroll
+      for (int t = 0; t < kPer; ++t) load_lds16(rs, l0 + t * 1024, min(cp_row[t], last) * RB + col[t]);
+    }
+  };
 
-  f32x16 acc[D / 32];
+  // LDS read addresses (loop invariant). K operand of contraction step kk:
+  // row l32 of the tile, chunk 2 kk + g. V^T operand of feature block db:
+  // transposing reads of rows 4g + s/4 (+ 16 h, + 8), columns
+  // db*32 + 16*((lane/16)%2) + 4*(s%4), s = lane % 16.
+  uint32_t k_off[KK], v_off[DB];
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.f;
+  for (int kk = 0; kk < KK; ++kk) k_off[kk] = l32 * RB + ((2 * kk + g) ^ Swz::k(l32)) * 16;
+  {
+    const int s = lane & 15, gp = (lane >> 4) & 1;
+    const int row = g * 4 + (s >> 2);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int ch = db * 4 + 2 * gp + ((s >> 1) & 1);
+      v_off[db] = row * RB + (ch ^ Swz::v(row)) * 16 + (s & 1) * 8;
+    }
+  }
+
+  // This lane's query rows (one per block); rows past the end load row N-1
+  // and are not stored. The query loads are issued before any copy (the
+  // scheduling barrier keeps them there), so the copy counts below are the
+  // last operations in the vector-memory queue.
+  int q_row[QB];
+  u32x4 qf[QB][KK];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    q_row[qb] = qt * BR + (wave * QB + qb) * 32 + l32;
+    const int q_ld = q_row[qb] < N ? q_row[qb] : N - 1;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) qf[qb][kk] = ld_global16(Q + ((int64_t)q_ld * D + kk * 16 + g * 8) * 2);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
   const int n_tiles = (N + BC - 1) / BC;
-
-  KS ks;
-  VS vs;
-  ks.load(K, 0, N, tid);
-  vs.load(reinterpret_cast<const uint16_t*>(V), 0, N, tid);
-  ks.store(smem, tid);
-  vs.store(smem + KS::kBytes, tid);
-  __syncthreads();
-
-  // One K/V tile: scores, online-softmax update, P V. Only the last tile can
-  // hold keys past N; MASK is true for that one alone.
-  auto step = [&](int j, auto mask_tag) {
-    constexpr bool MASK = decltype(mask_tag)::value;
-    const char* kbuf = smem + (j & 1) * kStage;
-    const char* vbuf = kbuf + KS::kBytes;
-    const bool more = j + 1 < n_tiles;
-    if (more) {
-      ks.load(K, (j + 1) * BC, N, tid);
-      vs.load(reinterpret_cast<const uint16_t*>(V), (j + 1) * BC, N, tid);
+  const int n_full = N / BC;
+  // Ring start: tiles 0..2 of K and V.
+  for (int t = 0; t < 3; ++t)
+    if (t < n_tiles) {
+      copy_tile(K, t, kbuf(t), cp_k);
+      copy_tile(V, t, vbuf(t), cp_v);
     }
 
-    // S^T = K Q^T for this tile: NS blocks of 32 keys x 32 queries.
-    f32x16 s[NS];
+  f32x16 acc[QB][DB];
+  float l_run[QB], m_run[QB];
 #pragma unroll
-    for (int kb = 0; kb < NS; ++kb) s[kb] = f32x16{};
+  for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk)
-#pragma unroll
-      for (int kb = 0; kb < NS; ++kb)
-        s[kb] = Mfma<E>::run(KS::read16(kbuf, kb * 32 + l32, (kk * 16 + g * 8) * 2), qf[kk], s[kb]);
+    for (int db = 0; db < DB; ++db) acc[qb][db] = f32x16{};
+    l_run[qb] = 0.f;
+  }
+  const float hide = c >= 0.f ? -INFINITY : INFINITY;
+  typedef f32x16 Scores[QB];
 
-    const int key0 = j * BC;
-    if constexpr (MASK) hide_tail(s, key0, N, g, c >= 0.f ? -INFINITY : INFINITY);
-
-    float alpha;
-    if (update_max(row_max_scaled(s, c), m_run, l_run, alpha)) {
+  // S^T = K Q^T for one tile (32 keys x 32 queries per block).
+  auto scores = [&](const char* kb_lds, Scores& s) {
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) acc[db] *= alpha;
+    for (int qb = 0; qb < QB; ++qb) s[qb] = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const u32x4 a = *reinterpret_cast<const u32x4*>(kb_lds + k_off[kk]);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) s[qb] = Mfma<E>::run(a, qf[qb][kk], s[qb]);
     }
-
-    // Probabilities, rounded to the element type: B operand of O^T += V^T P^T.
-    // Register r of block kb is key slot (r % 8) of half (r / 8) of that block.
-    u32x4 pf[NS][2];
-    float lsum = 0.f;
-    const float neg_m = -m_run;
+  };
+  // Probabilities of one tile, rounded to the element type: the B operand of
+  // O^T += V^T P^T (register r is key slot r % 8 of half r / 8). Their float32
+  // sum (before rounding: the row normaliser and LSE are float32) goes to l.
+  auto probs = [&](const Scores& s, u32x4(&pf)[QB][2], int key0, bool mask) {
 #pragma unroll
-    for (int kb = 0; kb < NS; ++kb)
+    for (int qb = 0; qb < QB; ++qb) {
+      float ls[2] = {0.f, 0.f};
+      const float neg_m = -m_run[qb];
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
           const int r = h * 8 + 2 * w;
-          float p0 = exp2_fast(fmaf(s[kb][r], c, neg_m));
-          float p1 = exp2_fast(fmaf(s[kb][r + 1], c, neg_m));
-          if constexpr (MASK) {
+          float p0 = exp2_fast(fmaf(s[qb][r], c, neg_m));
+          float p1 = exp2_fast(fmaf(s[qb][r + 1], c, neg_m));
+          if (mask) {
             // explicit zero: with c == 0 a hidden score would give 0 * inf
-            if (key0 + score_key(kb, r, g) >= N) p0 = 0.f;
-            if (key0 + score_key(kb, r + 1, g) >= N) p1 = 0.f;
+            if (key0 + score_key(0, r, g) >= N) p0 = 0.f;
+            if (key0 + score_key(0, r + 1, g) >= N) p1 = 0.f;
           }
-          lsum += p0 + p1;
-          pf[kb][h][w] = Mfma<E>::pack2(p0, p1);
+          pf[qb][h][w] = Mfma<E>::pack2(p0, p1);
+          ls[h] += p0 + p1;
         }
-    l_run += lsum;
-
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int kb = 0; kb < NS; ++kb)
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-          acc[db] = Mfma<E>::run(VS::read(vbuf, db * 32 + l32, kb * 32 + h * 16 + g * 8), pf[kb][h],
-                                 acc[db]);
-
-    if (more) {
-      char* nbuf = smem + ((j + 1) & 1) * kStage;
-      ks.store(nbuf, tid);
-      vs.store(nbuf + KS::kBytes, tid);
+      l_run[qb] += ls[0] + ls[1];
     }
-    __syncthreads();
   };
-  const int n_full = N / BC;
-  for (int j = 0; j < n_full; ++j) step(j, std::false_type{});
-  if (n_full < n_tiles) step(n_full, std::true_type{});
+  // O^T += V^T P^T for one tile.
+  auto accumulate = [&](const char* vb_lds, const u32x4(&pf)[QB][2]) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const char* a = vb_lds + v_off[db] + h * 16 * RB;
+        const u32x2 lo = lds_read_tr16(a), hi = lds_read_tr16(a + 8 * RB);
+        const u32x4 vt = {lo[0], lo[1], hi[0], hi[1]};
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) acc[qb][db] = Mfma<E>::run(vt, pf[qb][h], acc[qb][db]);
+      }
+  };
+  // Running maxima with the scores s of the next tile: moved lazily; the
+  // accumulator and the sum follow them.
+  auto advance_max = [&](const Scores& s) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const f32x16 one[1] = {s[qb]};
+      float alpha;
+      if (update_max(row_max_scaled(one, c), m_run[qb], l_run[qb], alpha)) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db) acc[qb][db] *= alpha;
+      }
+    }
+  };
+  auto mask_tail = [&](Scores& s, int key0) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      f32x16 one[1] = {s[qb]};
+      hide_tail(one, key0, N, g, hide);
+      s[qb] = one[0];
+    }
+  };
+
+  // Step 0 reads K_1 and V_0; tiles 0 and 1 have landed once at most the
+  // copies of tile 2 are in flight (vector-memory operations complete in
+  // issue order).
+  if (n_tiles > 2)
+    vm_wait<2 * kPer>();
+  else
+    vm_wait<0>();
+  __syncthreads();
+  Scores sa, sb;
+  scores(kbuf(0), sa);
+  if (n_tiles == 1 && N % BC) mask_tail(sa, 0);
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const f32x16 one[1] = {sa[qb]};
+    m_run[qb] = row_max_scaled(one, c);
+  }
+
+  // One step: tile j's probabilities and P V, tile j+1's scores and maximum.
+  // Copies of K_{j+3} and V_{j+3} go out first, into the buffers of tile
+  // j-1, which the previous barrier freed; at the end the copies of tiles
+  // j+2, issued one step earlier, must have landed before the barrier.
+  // STEADY: buffers known at compile time (B = j % NBUF), tile j+1 full,
+  // copies of this step exist. Otherwise everything is decided at run time.
+  auto step = [&](int j, Scores& s_cur, Scores& s_nxt, auto b_tag, auto steady_tag) {
+    constexpr bool STEADY = decltype(steady_tag)::value;
+    const int b = STEADY ? decltype(b_tag)::value : j % NBUF;
+    const bool copies = STEADY || j + 3 < n_tiles;
+    if (copies) {
+      copy_tile(K, j + 3, kbuf((b + 3) % NBUF), cp_k);
+      copy_tile(V, j + 3, vbuf((b + 3) % NBUF), cp_v);
+    }
+    const bool next = STEADY || j + 1 < n_tiles;
+    if (next) scores(kbuf((b + 1) % NBUF), s_nxt);
+    u32x4 pf[QB][2];
+    probs(s_cur, pf, j * BC, !STEADY && j == n_full);
+    accumulate(vbuf(b), pf);
+    if (next) {
+      if (!STEADY && j + 1 == n_full) mask_tail(s_nxt, (j + 1) * BC);  // tile j+1 is the ragged one
+      advance_max(s_nxt);
+      if (copies)
+        vm_wait<2 * kPer>();
+      else
+        vm_wait<0>();
+      __syncthreads();
+    }
+  };
+  using T = std::true_type;
+  using F = std::false_type;
+  int j = 0;
+  // steady groups: every step's copies exist (j + 3 + 3 < n_tiles) and the
+  // tile after the group's last one is full (j + 4 < n_full)
+  for (; j + 6 < n_tiles && j + 4 < n_full; j += 4) {
+    step(j, sa, sb, std::integral_constant<int, 0>{}, T{});
+    step(j + 1, sb, sa, std::integral_constant<int, 1>{}, T{});
+    step(j + 2, sa, sb, std::integral_constant<int, 2>{}, T{});
+    step(j + 3, sb, sa, std::integral_constant<int, 3>{}, T{});
+  }
+  for (; j < n_tiles; ++j) {
+    step(j, sa, sb, std::integral_constant<int, 0>{}, F{});
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) sa[qb] = sb[qb];
+  }
 
   // Epilogue: one division per row ("rescale once at the end"), O rounded to
   // nearest even; LSE = ln(2^m * l) = (m + log2 l) * ln 2.
-  const float l_tot = pair_sum(l_run);
-  const float inv = 1.f / l_tot;
-  if (q_row < N) {
-    char* orow = p.o + head + (int64_t)q_row * D * 2;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+  for (int qb = 0; qb < QB; ++qb) {
+    const float l_tot = pair_sum(l_run[qb]);
+    const float inv = 1.f / l_tot;
+    if (q_row[qb] < N) {
+      char* orow = p.o + head + (int64_t)q_row[qb] * RB;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        u32x2 w;
-        w[0] = Mfma<E>::pack2(acc[db][i * 4 + 0] * inv, acc[db][i * 4 + 1] * inv);
-        w[1] = Mfma<E>::pack2(acc[db][i * 4 + 2] * inv, acc[db][i * 4 + 3] * inv);
-        *reinterpret_cast<u32x2*>(orow + (db * 32 + i * 8 + g * 4) * 2) = w;
-      }
-    if (g == 0 && p.lse) p.lse[(int64_t)bh * N + q_row] = (m_run + log2f(l_tot)) * kLn2;
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          u32x2 w;
+          w[0] = Mfma<E>::pack2(acc[qb][db][i * 4 + 0] * inv, acc[qb][db][i * 4 + 1] * inv);
+          w[1] = Mfma<E>::pack2(acc[qb][db][i * 4 + 2] * inv, acc[qb][db][i * 4 + 3] * inv);
+          *reinterpret_cast<u32x2*>(orow + (db * 32 + i * 8 + g * 4) * 2) = w;
+        }
+      if (g == 0 && p.lse) p.lse[(int64_t)bh * N + q_row[qb]] = (m_run[qb] + log2f(l_tot)) * kLn2;
+    }
   }
 }
 
@@ -286,6 +430,7 @@ __global__ __launch_bounds__(NW * 64) void flash_fwd_f32(FwdParams p) {
   vs.load(V, 0, N, tid);
   ks.store(smem, tid);
   vs.store(smem + KS::kBytes, tid);
+  wait_vmem_all();
   __syncthreads();
 
   auto step = [&](int j, auto mask_tag) {
@@ -366,11 +511,12 @@ __global__ __launch_bounds__(NW * 64) void flash_fwd_f32(FwdParams p) {
 
 // Tile configuration per (element type, head size).
 constexpr int kWavesHalf = 4;
+constexpr int kQueryBlocksHalf = 1;
 constexpr int kWavesF32 = 4;
 
-template <class E, int D, int BC>
+template <class E, int D, int QB>
 hipError_t run_half(const AttnArgs& a) {
-  constexpr int BR = kWavesHalf * 32;
+  constexpr int BR = kWavesHalf * 32 * QB;
   FwdParams p;
   p.q = static_cast<const char*>(a.q);
   p.k = static_cast<const char*>(a.k);
@@ -381,7 +527,7 @@ hipError_t run_half(const AttnArgs& a) {
   p.n_qtiles = (a.N + BR - 1) / BR;
   p.n_blocks = a.B * a.H * p.n_qtiles;
   p.c = a.scale * kLog2e;
-  hipLaunchKernelGGL((flash_fwd_half<E, D, BC, kWavesHalf>), dim3(p.n_blocks), dim3(kWavesHalf * 64), 0,
+  hipLaunchKernelGGL((flash_fwd_half<E, D, kWavesHalf, QB>), dim3(p.n_blocks), dim3(kWavesHalf * 64), 0,
                      a.stream, p);
   return hipGetLastError();
 }
@@ -405,14 +551,14 @@ hipError_t run_f32(const AttnArgs& a) {
 
 }  // namespace
 
-int flash_rows_per_block(int dtype, int /*d*/) { return (dtype == kF32 ? kWavesF32 : kWavesHalf) * 32; }
+int flash_rows_per_block(int dtype, int /*d*/) { return dtype == kF32 ? kWavesF32 * 32 : kWavesHalf * 32 * kQueryBlocksHalf; }
 
 hipError_t launch_flash(const AttnArgs& a) {
   switch (a.dtype) {
     case kBF16:
-      return a.d == 128 ? run_half<BF16, 128, 64>(a) : run_half<BF16, 64, 128>(a);
+      return a.d == 128 ? run_half<BF16, 128, kQueryBlocksHalf>(a) : run_half<BF16, 64, kQueryBlocksHalf>(a);
     case kF16:
-      return a.d == 128 ? run_half<F16, 128, 64>(a) : run_half<F16, 64, 128>(a);
+      return a.d == 128 ? run_half<F16, 128, kQueryBlocksHalf>(a) : run_half<F16, 64, kQueryBlocksHalf>(a);
     default:
       return a.d == 128 ? run_f32<128>(a) : run_f32<64>(a);
   }
