@@ -118,6 +118,50 @@ def copy_calibration(nbytes: int, reps: int) -> None:
     print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps}), flush=True)
 
 
+SWEEP_N = (1024, 2048, 4096, 8192, 16384, 32768)
+
+
+def traffic_sweep(entry: str) -> None:
+    """Two launches (the first is a warm-up) of one entry point at each N in
+    SWEEP_N, B=1, H=16, d=128, bf16, inputs N(0,1) drawn on the GPU from a
+    fixed seed (traffic does not depend on the values). Run under
+    `rocprofv3 --pmc FETCH_SIZE` / `WRITE_SIZE`: the dispatches appear in this
+    order, one per flash launch and three per naive launch (all heads fit one
+    workspace chunk)."""
+    import torch
+
+    import io_aware_tiled_06_amd as fa
+
+    if not os.path.exists(fa.LIB_PATH):
+        import __graft_entry__
+
+        __graft_entry__.build()
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev).manual_seed(5)
+    for n in SWEEP_N:
+        shape = (1, 16, n, 128)
+        q, k, v = (torch.randn(shape, generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+                   for _ in range(3))
+        o = torch.empty_like(q)
+        ws = None
+        if entry == "naive":
+            ws = torch.empty(fa.attn_naive_workspace_bytes(1, 16, n, "bf16"), dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize(dev)
+        times = []
+        for _ in range(2):
+            t0 = time.perf_counter()
+            if entry == "naive":
+                fa.attn_naive_fwd(q, k, v, out=o, workspace=ws)
+            else:
+                fa.flash_attn_fwd(q, k, v, out=o)
+            torch.cuda.synchronize(dev)
+            times.append(time.perf_counter() - t0)
+        print(json.dumps({"sweep": entry, "N": n, "B": 1, "H": 16, "d": 128, "dtype": "bf16",
+                          "wall_ms": round(times[-1] * 1e3, 4)}), flush=True)
+        del q, k, v, o, ws
+        torch.cuda.empty_cache()
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -128,9 +172,14 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (counter calibration) and exit")
+    ap.add_argument("--traffic-sweep", choices=["flash", "naive"], default=None,
+                    help="only run the N sweep used for the traffic-versus-N counters and exit")
     args = ap.parse_args()
     if args.copy_calibration:
         copy_calibration(args.copy_calibration, 3)
+        return 0
+    if args.traffic_sweep:
+        traffic_sweep(args.traffic_sweep)
         return 0
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path",
