@@ -89,6 +89,19 @@ __device__ __forceinline__ float row_max_scaled(const f32x16 (&s)[NS], float c) 
   return e * c;
 }
 
+// The same with the sign of c known at compile time (NEG: c < 0), so that no
+// branch splits the code around it.
+template <bool NEG, int NS>
+__device__ __forceinline__ float row_max_scaled_fixed(const f32x16 (&s)[NS], float c) {
+  float e = s[0][0];
+#pragma unroll
+  for (int kb = 0; kb < NS; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) e = NEG ? fminf(e, s[kb][r]) : fmaxf(e, s[kb][r]);
+  e = NEG ? pair_min(e) : pair_max(e);
+  return e * c;
+}
+
 // Running-maximum update for one tile; returns true (wave-uniform) when the
 // accumulator must be multiplied by `alpha`.
 __device__ __forceinline__ bool update_max(float m_tile, float& m_run, float& l_run, float& alpha) {
@@ -118,7 +131,7 @@ __device__ __forceinline__ bool update_max(float m_tile, float& m_run, float& l_
 // tile j+1. One barrier per tile publishes the tiles two steps ahead and
 // frees the buffers the next copies overwrite.
 // ---------------------------------------------------------------------------
-template <class E, int D, int NW, int QB>
+template <class E, int D, int NW, int QB, bool NEG>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(QB == 1 ? 2 : 1)))
 void flash_fwd_half(FwdParams p) {
   constexpr int BR = NW * 32 * QB;
@@ -225,7 +238,8 @@ void flash_fwd_half(FwdParams p) {
     for (int db = 0; db < DB; ++db) acc[qb][db] = f32x16{};
     l_run[qb] = 0.f;
   }
-  const float hide = c >= 0.f ? -INFINITY : INFINITY;
+  // keys past N must lose the row extremum: -inf for c >= 0, +inf for c < 0
+  constexpr float hide = NEG ? INFINITY : -INFINITY;
   typedef f32x16 Scores[QB];
 
   // S^T = K Q^T for one tile (32 keys x 32 queries per block).
@@ -245,7 +259,7 @@ void flash_fwd_half(FwdParams p) {
   auto probs = [&](const Scores& s, u32x4(&pf)[QB][2], int key0, bool mask) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      float ls[2] = {0.f, 0.f};
+      float ls[2];
       const float neg_m = -m_run[qb];
 #pragma unroll
       for (int h = 0; h < 2; ++h)
@@ -260,7 +274,7 @@ void flash_fwd_half(FwdParams p) {
             if (key0 + score_key(0, r + 1, g) >= N) p1 = 0.f;
           }
           pf[qb][h][w] = Mfma<E>::pack2(p0, p1);
-          ls[h] += p0 + p1;
+          ls[h] = w == 0 ? p0 + p1 : ls[h] + (p0 + p1);
         }
       l_run[qb] += ls[0] + ls[1];
     }
@@ -285,7 +299,7 @@ void flash_fwd_half(FwdParams p) {
     for (int qb = 0; qb < QB; ++qb) {
       const f32x16 one[1] = {s[qb]};
       float alpha;
-      if (update_max(row_max_scaled(one, c), m_run[qb], l_run[qb], alpha)) {
+      if (update_max(row_max_scaled_fixed<NEG>(one, c), m_run[qb], l_run[qb], alpha)) {
 #pragma unroll
         for (int db = 0; db < DB; ++db) acc[qb][db] *= alpha;
       }
@@ -314,7 +328,7 @@ void flash_fwd_half(FwdParams p) {
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const f32x16 one[1] = {sa[qb]};
-    m_run[qb] = row_max_scaled(one, c);
+    m_run[qb] = row_max_scaled_fixed<NEG>(one, c);
   }
 
   // One step: tile j's probabilities and P V, tile j+1's scores and maximum.
@@ -527,8 +541,12 @@ hipError_t run_half(const AttnArgs& a) {
   p.n_qtiles = (a.N + BR - 1) / BR;
   p.n_blocks = a.B * a.H * p.n_qtiles;
   p.c = a.scale * kLog2e;
-  hipLaunchKernelGGL((flash_fwd_half<E, D, kWavesHalf, QB>), dim3(p.n_blocks), dim3(kWavesHalf * 64), 0,
-                     a.stream, p);
+  if (a.scale < 0.f)
+    hipLaunchKernelGGL((flash_fwd_half<E, D, kWavesHalf, QB, true>), dim3(p.n_blocks), dim3(kWavesHalf * 64), 0,
+                       a.stream, p);
+  else
+    hipLaunchKernelGGL((flash_fwd_half<E, D, kWavesHalf, QB, false>), dim3(p.n_blocks), dim3(kWavesHalf * 64), 0,
+                       a.stream, p);
   return hipGetLastError();
 }
 
