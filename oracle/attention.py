@@ -18,6 +18,10 @@ Sources (the pages, by title and section):
 
 Readings taken where the pages are silent (each also listed with the design
 notes of this repository):
+  * causal (prefill) attention: the pages name the prefill case ("FlashAttention,
+    simplified", "Why it matters for inference") but no mask; the plainest
+    reading is the lower-triangular one -- query i of a sequence sees keys
+    j <= i (the mask is aligned at the first token, N_q = N_k).
   * scale: the scores are ``scale * q_i . k_j`` with ``scale`` a caller value
     (the pages say "scaled" but give no value); workloads use 1/sqrt(d).
   * logsumexp: LSE_i = m_i + ln(l_i) in natural log of the scaled scores.  It is
@@ -54,7 +58,7 @@ def _check(q, k, v):
         raise ValueError("k and v must have the same number of rows")
 
 
-def attention_reference(q, k, v, scale: float):
+def attention_reference(q, k, v, scale: float, causal: bool = False):
     """Exact attention by its definition, in float64, with complete score rows.
 
     For each leading index (batch, head) and each query row i:
@@ -71,6 +75,9 @@ def attention_reference(q, k, v, scale: float):
     Returns (O float64 [..., Nq, dv], LSE float64 [..., Nq]). Rows are handled
     in blocks of complete rows, which leaves the row-wise definition unchanged.
     With Nk == 0 the softmax is undefined and a ValueError is raised.
+
+    causal=True: row i's softmax runs over the keys j <= i only (S_ij = -inf
+    for j > i, whose exponential is exactly 0); requires Nq == Nk.
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
     _check(q, k, v)
@@ -78,6 +85,8 @@ def attention_reference(q, k, v, scale: float):
     nq, nk, dv = q.shape[-2], k.shape[-2], v.shape[-1]
     if nk == 0 and nq > 0:
         raise ValueError("softmax over zero keys is undefined")
+    if causal and nq != nk:
+        raise ValueError("causal attention needs as many queries as keys")
     s = np.float64(scale)
     out = np.empty(lead + (nq, dv), dtype=np.float64)
     lse = np.empty(lead + (nq,), dtype=np.float64)
@@ -87,6 +96,8 @@ def attention_reference(q, k, v, scale: float):
         for r0 in range(0, nq, rows):
             r1 = min(nq, r0 + rows)
             scores = s * (qh[r0:r1] @ kh.T)
+            if causal:
+                scores[_future(r0, r1, nk)] = -np.inf
             m = scores.max(axis=1)
             e = np.exp(scores - m[:, None])
             l = e.sum(axis=1)
@@ -96,7 +107,15 @@ def attention_reference(q, k, v, scale: float):
     return out, lse
 
 
-def attention_probabilities(q, k, scale: float):
+def _future(r0, r1, nk):
+    """Boolean mask of the keys a causal row may not see: rows r0..r1-1
+    (absolute query index i), columns j > i."""
+    i = np.arange(r0, r1)[:, None]
+    j = np.arange(nk)[None, :]
+    return j > i
+
+
+def attention_probabilities(q, k, scale: float, causal: bool = False):
     """The softmax matrix P = softmax(scale * q k^T) row by row, float64.
 
     Same definition as ``attention_reference``; materialises P, so it is meant
@@ -106,12 +125,16 @@ def attention_probabilities(q, k, scale: float):
     if q.ndim < 2 or k.shape[:-2] != q.shape[:-2] or k.shape[-1] != q.shape[-1]:
         raise ValueError("q and k shapes do not match")
     scores = np.float64(scale) * (q @ np.swapaxes(k, -1, -2))
+    if causal:
+        if q.shape[-2] != k.shape[-2]:
+            raise ValueError("causal attention needs as many queries as keys")
+        scores[..., _future(0, q.shape[-2], k.shape[-2])] = -np.inf
     m = scores.max(axis=-1, keepdims=True)
     e = np.exp(scores - m)
     return e / e.sum(axis=-1, keepdims=True)
 
 
-def attention_online(q, k, v, scale: float, block: int):
+def attention_online(q, k, v, scale: float, block: int, causal: bool = False):
     """The pages' streaming algorithm over K/V blocks, in float64.
 
     "FlashAttention, simplified", "The trick": starting from m = -inf, l = 0,
@@ -125,6 +148,8 @@ def attention_online(q, k, v, scale: float, block: int):
         m     = m_new
     and finally O = acc / l.  LSE = m + ln l (the same reading as above).
     All query rows are carried together: query rows never interact.
+    causal=True: scores of keys j > i are -inf in every block (they add
+    exp(-inf) = 0); block 0 holds key 0, so no row starts from an empty block.
     Returns (O, LSE) like ``attention_reference``.
     """
     if block < 1:
@@ -135,6 +160,8 @@ def attention_online(q, k, v, scale: float, block: int):
     nq, nk, dv = q.shape[-2], k.shape[-2], v.shape[-1]
     if nk == 0 and nq > 0:
         raise ValueError("softmax over zero keys is undefined")
+    if causal and nq != nk:
+        raise ValueError("causal attention needs as many queries as keys")
     s = np.float64(scale)
     out = np.empty(lead + (nq, dv), dtype=np.float64)
     lse = np.empty(lead + (nq,), dtype=np.float64)
@@ -146,6 +173,8 @@ def attention_online(q, k, v, scale: float, block: int):
         for j0 in range(0, nk, block):
             j1 = min(nk, j0 + block)
             scores = s * (qh @ kh[j0:j1].T)
+            if causal:
+                scores[np.arange(j0, j1)[None, :] > np.arange(nq)[:, None]] = -np.inf
             m_new = np.maximum(m, scores.max(axis=1))
             alpha = np.exp(m - m_new)
             e = np.exp(scores - m_new[:, None])

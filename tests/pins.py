@@ -23,11 +23,12 @@ from decimal import Decimal, localcontext
 import numpy as np
 
 
-def decimal_attention(q, k, v, scale, prec: int = 40):
+def decimal_attention(q, k, v, scale, prec: int = 40, causal: bool = False):
     """Attention of one head by brute force in ``prec``-digit decimal arithmetic.
 
     q [N, d], k [M, d], v [M, dv]; values and scale are converted exactly from
-    binary floating point. Returns (O, LSE) as float64 arrays.
+    binary floating point. Returns (O, LSE) as float64 arrays. causal=True:
+    query i uses keys 0..i only.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -42,12 +43,13 @@ def decimal_attention(q, k, v, scale, prec: int = 40):
         out = np.empty((n, dv))
         lse = np.empty(n)
         for i in range(n):
-            s = [sc * sum(Q[i][t] * K[j][t] for t in range(len(Q[i]))) for j in range(m)]
+            keys = range(i + 1) if causal else range(m)
+            s = [sc * sum(Q[i][t] * K[j][t] for t in range(len(Q[i]))) for j in keys]
             mx = max(s)
             e = [(x - mx).exp() for x in s]
             z = sum(e)
             for c in range(dv):
-                out[i, c] = float(sum(e[j] * V[j][c] for j in range(m)) / z)
+                out[i, c] = float(sum(e[j] * V[j][c] for j in range(len(e))) / z)
             lse[i] = float(mx + z.ln())
     return out, lse
 
@@ -262,10 +264,99 @@ ALL_PINS = [
 ]
 
 
-def failing_pins(fn):
+# ---------------------------------------------------------------------------
+# Causal (prefill) attention: query i sees keys j <= i. Each pin takes
+# fn(q, k, v, scale) -> (O, LSE) computing causal attention.
+# ---------------------------------------------------------------------------
+
+
+def pin_causal_brute_force(fn, tol=1e-13):
+    """Tiny N against the decimal brute force over keys 0..i."""
+    for n, d in [(1, 3), (2, 4), (3, 4), (6, 5), (17, 8)]:
+        rng = _rng(300 + n + d)
+        q, k, v = (rng.standard_normal((n, d)) for _ in range(3))
+        for scale in (0.45, 2.0):
+            o, lse = fn(q[None], k[None], v[None], scale)
+            o_ref, lse_ref = decimal_attention(q, k, v, scale, causal=True)
+            assert np.max(np.abs(o[0] - o_ref)) <= tol, (n, d, scale, "O")
+            assert np.max(np.abs(lse[0] - lse_ref)) <= tol * max(1.0, np.max(np.abs(lse_ref))), (n, d, scale)
+
+
+def pin_causal_first_row(fn):
+    """Row 0 sees key 0 alone: O_0 = v_0 exactly and LSE_0 = scale q_0.k_0."""
+    rng = _rng(301)
+    q, k, v = (rng.standard_normal((2, 40, 16)) for _ in range(3))
+    o, lse = fn(q, k, v, 0.3)
+    assert np.max(np.abs(o[:, 0] - v[:, 0])) <= 1e-15
+    expect = 0.3 * np.einsum("bd,bd->b", q[:, 0], k[:, 0])
+    assert np.max(np.abs(lse[:, 0] - expect)) <= 1e-14
+
+
+def pin_causal_uniform(fn):
+    """scale = 0: row i is the mean of v_0..v_i and LSE_i = ln(i + 1)."""
+    rng = _rng(302)
+    n = 70
+    q, k, v = (rng.standard_normal((2, n, 8)) for _ in range(3))
+    o, lse = fn(q, k, v, 0.0)
+    prefix_mean = np.cumsum(v, axis=1) / np.arange(1, n + 1)[None, :, None]
+    assert np.max(np.abs(o - prefix_mean)) <= 1e-13
+    assert np.max(np.abs(lse - np.log(np.arange(1, n + 1))[None])) <= 1e-13
+
+
+def pin_causal_prefix(fn):
+    """No future token leaks: the first n rows of the full sequence equal the
+    causal attention of the sequence cut after n tokens, and changing a later
+    token leaves them unchanged."""
+    rng = _rng(303)
+    N = 60
+    q, k, v = (2.0 * rng.standard_normal((1, N, 12)) for _ in range(3))
+    o, lse = fn(q, k, v, 0.5)
+    for n in (1, 7, 33, 59):
+        o_n, lse_n = fn(q[:, :n], k[:, :n], v[:, :n], 0.5)
+        assert np.max(np.abs(o[:, :n] - o_n)) <= 1e-14, n
+        assert np.max(np.abs(lse[:, :n] - lse_n)) <= 1e-14, n
+    k2, v2 = k.copy(), v.copy()
+    k2[:, 40:] += 100.0
+    v2[:, 40:] -= 50.0
+    o2, lse2 = fn(q, k2, v2, 0.5)
+    assert np.max(np.abs(o2[:, :40] - o[:, :40])) <= 1e-14
+    assert np.max(np.abs(lse2[:, :40] - lse[:, :40])) <= 1e-14
+
+
+def pin_causal_library(fn):
+    """torch's CPU attention with is_causal=True and logsumexp over the
+    lower-triangular scores, float64."""
+    import torch
+    import torch.nn.functional as F
+
+    rng = _rng(304)
+    for (b, h, n, d) in ((1, 2, 45, 16), (2, 1, 129, 32)):
+        q, k, v = (rng.standard_normal((b, h, n, d)) for _ in range(3))
+        scale = 1.0 / math.sqrt(d)
+        o, lse = fn(q, k, v, scale)
+        tq, tk, tv = (torch.from_numpy(x) for x in (q, k, v))
+        with torch.no_grad():
+            o_t = F.scaled_dot_product_attention(tq, tk, tv, scale=scale, is_causal=True).numpy()
+            s_t = scale * (tq @ tk.transpose(-1, -2))
+            s_t = s_t.masked_fill(torch.ones(n, n, dtype=torch.bool).triu(1), float("-inf"))
+            lse_t = torch.logsumexp(s_t, dim=-1).numpy()
+        assert np.max(np.abs(o - o_t)) <= 1e-12, (b, h, n, d)
+        assert np.max(np.abs(lse - lse_t)) <= 1e-12, (b, h, n, d)
+
+
+CAUSAL_PINS = [
+    pin_causal_brute_force,
+    pin_causal_first_row,
+    pin_causal_uniform,
+    pin_causal_prefix,
+    pin_causal_library,
+]
+
+
+def failing_pins(fn, pins=None):
     """Names of the pins that ``fn`` fails (an exception counts as a failure)."""
     bad = []
-    for pin in ALL_PINS:
+    for pin in ALL_PINS if pins is None else pins:
         try:
             with np.errstate(all="ignore"):
                 pin(fn)

@@ -109,3 +109,56 @@ def test_unmutated_copy_passes():
     assert failing_pins(lambda q, k, v, s: _mutant(q, k, v, s, "none")) == []
     assert failing_pins(lambda q, k, v, s: _online_mutant(
         np.asarray(q, float), np.asarray(k, float), np.asarray(v, float), float(s), "online_none", 7)) == []
+
+
+# -- causal mask mistakes --------------------------------------------------------
+
+from pins import CAUSAL_PINS  # noqa: E402
+
+CAUSAL_MUTATIONS = ["exclude_diagonal", "upper_triangle", "one_key_ahead", "no_mask", "mask_rows_not_keys"]
+
+
+def _causal_mutant(q, k, v, scale, mutation):
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    n = q.shape[-2]
+    scores = float(scale) * (q @ np.swapaxes(k, -1, -2))
+    i = np.arange(n)[:, None]
+    j = np.arange(k.shape[-2])[None, :]
+    hidden = {
+        "exclude_diagonal": j >= i,
+        "upper_triangle": j < i,
+        "one_key_ahead": j > i + 1,
+        "no_mask": np.zeros((n, k.shape[-2]), dtype=bool),
+        "mask_rows_not_keys": i[::-1] < j,
+    }[mutation]
+    scores = np.where(hidden, -np.inf, scores)
+    m = scores.max(axis=-1, keepdims=True)
+    e = np.exp(scores - m)
+    l = e.sum(axis=-1, keepdims=True)
+    return (e / l) @ v, (m + np.log(l))[..., 0]
+
+
+@pytest.mark.parametrize("mutation", CAUSAL_MUTATIONS)
+def test_causal_mutant_is_caught(mutation):
+    bad = failing_pins(lambda q, k, v, s: _causal_mutant(q, k, v, s, mutation), CAUSAL_PINS)
+    assert bad, f"causal mutation {mutation} passed every causal pin"
+
+
+def test_causal_mutant_harness_is_sound():
+    """The unmutated harness (mask j > i) passes every causal pin."""
+
+    def correct(q, k, v, s):
+        q = np.asarray(q, dtype=np.float64)
+        k = np.asarray(k, dtype=np.float64)
+        v = np.asarray(v, dtype=np.float64)
+        n = q.shape[-2]
+        scores = float(s) * (q @ np.swapaxes(k, -1, -2))
+        scores = np.where(np.arange(n)[None, :] > np.arange(n)[:, None], -np.inf, scores)
+        m = scores.max(axis=-1, keepdims=True)
+        e = np.exp(scores - m)
+        l = e.sum(axis=-1, keepdims=True)
+        return (e / l) @ v, (m + np.log(l))[..., 0]
+
+    assert failing_pins(correct, CAUSAL_PINS) == []

@@ -6,7 +6,7 @@ import numpy as np
 import pytest
 
 from oracle import attention_online, attention_probabilities, attention_reference
-from pins import ALL_PINS, decimal_attention, support_function_bounds
+from pins import ALL_PINS, CAUSAL_PINS, decimal_attention, support_function_bounds
 
 
 @pytest.mark.parametrize("pin", ALL_PINS, ids=lambda p: p.__name__)
@@ -94,3 +94,45 @@ def test_support_function_detects_outside_point():
     outside = np.array([[[0.8, 0.8]]])
     assert support_function_bounds(inside, v) <= 0.0
     assert support_function_bounds(outside, v) > 0.0
+
+
+# -- causal (prefill) attention ------------------------------------------------
+
+@pytest.mark.parametrize("pin", CAUSAL_PINS, ids=lambda p: p.__name__)
+def test_causal_reference_meets_pin(pin):
+    pin(lambda q, k, v, s: attention_reference(q, k, v, s, causal=True))
+
+
+@pytest.mark.parametrize("block", [1, 7, 128])
+@pytest.mark.parametrize("pin", CAUSAL_PINS, ids=lambda p: p.__name__)
+def test_causal_online_meets_pin(pin, block):
+    pin(lambda q, k, v, s: attention_online(q, k, v, s, block, causal=True))
+
+
+@pytest.mark.parametrize("block", [1, 5, 32, 128, 300])
+def test_causal_tiling_invariance(block):
+    """The streaming loop with the causal mask over any tiling gives the
+    definition's result to 1e-12 (blocks straddling the diagonal included)."""
+    rng = np.random.default_rng(21)
+    q, k, v = (rng.standard_normal((2, 300, 32)) for _ in range(3))
+    q *= 3.0
+    o_ref, lse_ref = attention_reference(q, k, v, 1 / math.sqrt(32), causal=True)
+    o, lse = attention_online(q, k, v, 1 / math.sqrt(32), block, causal=True)
+    assert np.max(np.abs(o - o_ref)) <= 1e-12
+    assert np.max(np.abs(lse - lse_ref)) <= 1e-12
+
+
+def test_causal_probabilities_are_lower_triangular():
+    rng = np.random.default_rng(22)
+    q, k = (3.0 * rng.standard_normal((2, 90, 16)) for _ in range(2))
+    p = attention_probabilities(q, k, 0.3, causal=True)
+    assert np.all(np.triu(p, 1) == 0.0)
+    assert np.all(p >= 0.0)
+    assert np.max(np.abs(p.sum(axis=-1) - 1.0)) <= 1e-14
+
+
+def test_causal_needs_square():
+    q = np.zeros((1, 3, 4))
+    k = np.zeros((1, 5, 4))
+    with pytest.raises(ValueError):
+        attention_reference(q, k, k, 1.0, causal=True)
