@@ -169,6 +169,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="n32768_d128_bf16")
     ap.add_argument("--entry", choices=["flash", "naive"], default="flash")
+    ap.add_argument("--causal", action="store_true",
+                    help="time the causal entry point (query i sees keys 0..i); FLOPs count visible pairs only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (counter calibration) and exit")
@@ -205,12 +207,15 @@ def main() -> int:
     tq, tk, tv = (torch.from_numpy(x).to(tdt).to(dev) for x in (q, k, v))
     o = torch.empty_like(tq)
     ws = None
+    if args.causal and args.entry != "flash":
+        print("--causal applies to the fused entry point only", file=sys.stderr)
+        return 2
     if args.entry == "naive":
         nbytes = fa.attn_naive_workspace_bytes(w.B, w.H, w.N, w.dtype)
         ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
         step = lambda: fa.attn_naive_fwd(tq, tk, tv, w.scale, out=o, workspace=ws)  # noqa: E731
     else:
-        step = lambda: fa.flash_attn_fwd(tq, tk, tv, w.scale, out=o)  # noqa: E731
+        step = lambda: fa.flash_attn_fwd(tq, tk, tv, w.scale, causal=args.causal, out=o)  # noqa: E731
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -231,12 +236,14 @@ def main() -> int:
     ev_ms = [a.elapsed_time(b) for a, b in ev]
 
     flops = traffic.attention_flops(w.B, w.H, w.N, w.d)
+    if args.causal:  # visible (query, key) pairs: N (N + 1) / 2 per head
+        flops = 2.0 * w.B * w.H * w.N * (w.N + 1) * w.d
     ms_per_step = wall / args.steps * 1e3
     value = flops / (ms_per_step * 1e-3) / 1e12
     kern_ms = float(np.mean(ev_ms))
     achieved = flops / (kern_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
-    hbm = measured_traffic(w.name, args.entry)
+    hbm = None if args.causal else measured_traffic(w.name, args.entry)
     line = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -250,7 +257,8 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic",
-        "config": {"workload": w.name, "entry": args.entry, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+        "config": {"workload": w.name, "entry": args.entry, "causal": bool(args.causal), "B": w.B, "H": w.H,
+                   "N": w.N, "d": w.d,
                    "qk_sigma": w.qk_sigma, "seed": w.seed, "scale": w.scale},
         "pct_of_peak": round(100.0 * value / peak, 2),
         "roofline": {

@@ -82,6 +82,20 @@ int flash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* 
                    int B, int H, int N, int d, float scale, int dtype, void* stream);
 
 /*
+ * flash_attn_fwd_causal -- the fused forward pass with causal (prefill)
+ * masking: query i of a sequence attends keys 0..i only, i.e. row i's softmax
+ * and LSE run over S_i0 .. S_ii. The pages name the prefill case
+ * ("FlashAttention, simplified", "Why it matters for inference") but no mask;
+ * this is the lower-triangular reading, with queries and keys indexed from
+ * the same first token (N queries, N keys).
+ * Arguments, layout, arithmetic, determinism and errors as flash_attn_fwd.
+ * Key tiles entirely after a query tile are skipped, so the work is about
+ * half that of flash_attn_fwd.
+ */
+int flash_attn_fwd_causal(const void* q, const void* k, const void* v, void* o, float* lse,
+                          int B, int H, int N, int d, float scale, int dtype, void* stream);
+
+/*
  * attn_naive_workspace_bytes -- workspace for attn_naive_fwd to process every
  * head in one pass: B*H*N*N*(4 + e) bytes, e = element size of dtype (S is
  * held in float32, P in the input type). Any workspace of at least one head,

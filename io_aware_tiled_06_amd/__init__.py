@@ -34,7 +34,8 @@ __all__ = [
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libflashattn.so")
-EXPORTED_SYMBOLS = ("flash_attn_fwd", "attn_naive_workspace_bytes", "attn_naive_fwd", "fa_strerror")
+EXPORTED_SYMBOLS = ("flash_attn_fwd", "flash_attn_fwd_causal", "attn_naive_workspace_bytes", "attn_naive_fwd",
+                    "fa_strerror")
 
 # fa_status values (include/flash_attn.h)
 FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED = 0, 1, 2, 3
@@ -64,6 +65,8 @@ def lib() -> ctypes.CDLL:
         vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
         L.flash_attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
         L.flash_attn_fwd.restype = i
+        L.flash_attn_fwd_causal.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
+        L.flash_attn_fwd_causal.restype = i
         L.attn_naive_workspace_bytes.argtypes = [i, i, i, i]
         L.attn_naive_workspace_bytes.restype = sz
         L.attn_naive_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, sz, vp]
@@ -133,11 +136,12 @@ def _stream_ptr(q, stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def flash_attn_fwd(q, k, v, scale=None, *, out=None, return_lse=True, stream=None):
+def flash_attn_fwd(q, k, v, scale=None, *, causal=False, out=None, return_lse=True, stream=None):
     """Fused tiled attention forward pass on the GPU.
 
     q, k, v: contiguous [B, H, N, d] tensors (float32, float16 or bfloat16) on
     one GPU; d in {64, 128}. scale defaults to 1/sqrt(d) rounded to float32.
+    causal=True calls flash_attn_fwd_causal (query i sees keys 0..i).
     Returns (o, lse): o like q, lse float32 [B, H, N] (None if not requested).
     The call is asynchronous on ``stream`` (default: the current stream).
     """
@@ -147,12 +151,12 @@ def flash_attn_fwd(q, k, v, scale=None, *, out=None, return_lse=True, stream=Non
     B, H, N, d = q.shape
     s = _default_scale(d) if scale is None else float(scale)
     o, lse = _outputs(q, out, return_lse)
+    fn = lib().flash_attn_fwd_causal if causal else lib().flash_attn_fwd
     with torch.cuda.device(q.device):
-        st = lib().flash_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
-                                  lse.data_ptr() if lse is not None else None,
-                                  B, H, N, d, s, _dtype_code(q), _stream_ptr(q, stream))
+        st = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr() if lse is not None else None,
+                B, H, N, d, s, _dtype_code(q), _stream_ptr(q, stream))
     if st != FA_OK:
-        raise FlashAttnError(st, "flash_attn_fwd")
+        raise FlashAttnError(st, "flash_attn_fwd_causal" if causal else "flash_attn_fwd")
     return o, lse
 
 

@@ -72,6 +72,15 @@ int flash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* 
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+int flash_attn_fwd_causal(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
+                          int d, float scale, int dtype, void* stream) {
+  bool empty;
+  const int st = validate(q, k, v, o, lse, B, H, N, d, scale, dtype, &empty);
+  if (st != FA_OK || empty) return st;
+  const hipError_t e = fa::launch_flash_causal(make_args(q, k, v, o, lse, B, H, N, d, scale, dtype, stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 size_t attn_naive_workspace_bytes(int B, int H, int N, int dtype) {
   if (B < 0 || H < 0 || N < 0) return 0;
   if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16) return 0;

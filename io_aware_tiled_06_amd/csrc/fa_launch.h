@@ -30,6 +30,8 @@ int flash_rows_per_block(int dtype, int d);
 
 // Fused tiled forward pass over all B*H heads (one launch).
 hipError_t launch_flash(const AttnArgs& a);
+// The same with causal masking: query i sees keys j <= i.
+hipError_t launch_flash_causal(const AttnArgs& a);
 
 // Largest number of heads one launch of the three-pass path may cover
 // (grid-size limit); 0 means N is too large for that path.

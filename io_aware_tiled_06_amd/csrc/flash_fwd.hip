@@ -68,6 +68,17 @@ __device__ __forceinline__ void hide_tail(f32x16 (&s)[NS], int key0, int n, int 
       if (key0 + score_key(kb, r, g) >= n) s[kb][r] = hide;
 }
 
+// Hide keys past `lim` (this lane's last visible key) in a tile starting at
+// key0: they must lose the row extremum.
+template <int NS>
+__device__ __forceinline__ void hide_after(f32x16 (&s)[NS], int key0, int lim, int g, float hide) {
+#pragma unroll
+  for (int kb = 0; kb < NS; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (key0 + score_key(kb, r, g) > lim) s[kb][r] = hide;
+}
+
 // max over the row's keys of c*s, for the two lanes of a pair (same query row).
 // For c < 0 the maximum of c*s is c times the minimum of s.
 template <int NS>
@@ -131,9 +142,10 @@ __device__ __forceinline__ bool update_max(float m_tile, float& m_run, float& l_
 // tile j+1. One barrier per tile publishes the tiles two steps ahead and
 // frees the buffers the next copies overwrite.
 // ---------------------------------------------------------------------------
-template <class E, int D, int NW, int QB, bool NEG>
+template <class E, int D, int NW, int QB, bool NEG, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(QB == 1 ? 2 : 1)))
 void flash_fwd_half(FwdParams p) {
+  static_assert(!CAUSAL || QB == 1, "causal masking assumes one 32-row block per wave");
   constexpr int BR = NW * 32 * QB;
   constexpr int BC = 32;
   constexpr int NBUF = 4;
@@ -152,7 +164,9 @@ void flash_fwd_half(FwdParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, g = lane >> 5;
   const int blk = xcd_remap(blockIdx.x, p.n_blocks);
-  const int bh = blk / p.n_qtiles, qt = blk % p.n_qtiles;
+  const int bh = blk / p.n_qtiles;
+  // causal: the last query tiles of a head have the most keys; start them first
+  const int qt = CAUSAL ? p.n_qtiles - 1 - blk % p.n_qtiles : blk % p.n_qtiles;
   const int N = p.n;
   const int64_t head = (int64_t)bh * N * RB;  // bytes
   const char* Q = p.q + head;
@@ -223,9 +237,18 @@ void flash_fwd_half(FwdParams p) {
 
   const int n_tiles = (N + BC - 1) / BC;
   const int n_full = N / BC;
+  // Key tiles this workgroup visits: all of them, or (causal) up to the one
+  // holding its last query row. This wave stops at its own last tile: for
+  // causal attention the diagonal tile `diag` (its 32 rows start at key
+  // 32 diag), where keys after each row's own position are hidden; and
+  // `key_lim` is this lane's last visible key.
+  const int kt_end = CAUSAL ? min(n_tiles, (qt + 1) * (BR / BC)) : n_tiles;
+  const int diag = CAUSAL ? (qt * BR + wave * 32) / BC : n_tiles;
+  const int my_last = min(diag, n_tiles - 1);
+  const int key_lim = CAUSAL ? min(q_row[0], N - 1) : N - 1;
   // Ring start: tiles 0..2 of K and V.
   for (int t = 0; t < 3; ++t)
-    if (t < n_tiles) {
+    if (t < kt_end) {
       copy_tile(K, t, kbuf(t), cp_k);
       copy_tile(V, t, vbuf(t), cp_v);
     }
@@ -270,8 +293,8 @@ void flash_fwd_half(FwdParams p) {
           float p1 = exp2_fast(fmaf(s[qb][r + 1], c, neg_m));
           if (mask) {
             // explicit zero: with c == 0 a hidden score would give 0 * inf
-            if (key0 + score_key(0, r, g) >= N) p0 = 0.f;
-            if (key0 + score_key(0, r + 1, g) >= N) p1 = 0.f;
+            if (key0 + score_key(0, r, g) > key_lim) p0 = 0.f;
+            if (key0 + score_key(0, r + 1, g) > key_lim) p1 = 0.f;
           }
           pf[qb][h][w] = Mfma<E>::pack2(p0, p1);
           ls[h] = w == 0 ? p0 + p1 : ls[h] + (p0 + p1);
@@ -309,22 +332,24 @@ void flash_fwd_half(FwdParams p) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       f32x16 one[1] = {s[qb]};
-      hide_tail(one, key0, N, g, hide);
+      hide_after(one, key0, key_lim, g, hide);
       s[qb] = one[0];
     }
   };
+  // Tiles that need masking: the ragged last one, and (causal) the diagonal.
+  auto needs_mask = [&](int t) { return t == n_full || (CAUSAL && t == diag); };
 
   // Step 0 reads K_1 and V_0; tiles 0 and 1 have landed once at most the
   // copies of tile 2 are in flight (vector-memory operations complete in
   // issue order).
-  if (n_tiles > 2)
+  if (kt_end > 2)
     vm_wait<2 * kPer>();
   else
     vm_wait<0>();
   __syncthreads();
   Scores sa, sb;
   scores(kbuf(0), sa);
-  if (n_tiles == 1 && N % BC) mask_tail(sa, 0);
+  if (needs_mask(0)) mask_tail(sa, 0);
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const f32x16 one[1] = {sa[qb]};
@@ -335,24 +360,33 @@ void flash_fwd_half(FwdParams p) {
   // Copies of K_{j+3} and V_{j+3} go out first, into the buffers of tile
   // j-1, which the previous barrier freed; at the end the copies of tiles
   // j+2, issued one step earlier, must have landed before the barrier.
-  // STEADY: buffers known at compile time (B = j % NBUF), tile j+1 full,
-  // copies of this step exist. Otherwise everything is decided at run time.
+  // STEADY: buffers known at compile time (B = j % NBUF), tile j+1 needs no
+  // mask for any wave, copies of this step exist. Otherwise everything is
+  // decided at run time; the workgroup-wide decisions (copies, barrier) and
+  // this wave's own (does it still work on tile j, j+1) are kept apart, so
+  // every wave passes the same barriers.
   auto step = [&](int j, Scores& s_cur, Scores& s_nxt, auto b_tag, auto steady_tag) {
     constexpr bool STEADY = decltype(steady_tag)::value;
     const int b = STEADY ? decltype(b_tag)::value : j % NBUF;
-    const bool copies = STEADY || j + 3 < n_tiles;
+    const bool copies = STEADY || j + 3 < kt_end;
     if (copies) {
       copy_tile(K, j + 3, kbuf((b + 3) % NBUF), cp_k);
       copy_tile(V, j + 3, vbuf((b + 3) % NBUF), cp_v);
     }
-    const bool next = STEADY || j + 1 < n_tiles;
+    const bool wg_next = STEADY || j + 1 < kt_end;
+    const bool next = STEADY || j + 1 <= my_last;
+    const bool cur = STEADY || j <= my_last;
     if (next) scores(kbuf((b + 1) % NBUF), s_nxt);
-    u32x4 pf[QB][2];
-    probs(s_cur, pf, j * BC, !STEADY && j == n_full);
-    accumulate(vbuf(b), pf);
+    if (cur) {
+      u32x4 pf[QB][2];
+      probs(s_cur, pf, j * BC, !STEADY && needs_mask(j));
+      accumulate(vbuf(b), pf);
+    }
     if (next) {
-      if (!STEADY && j + 1 == n_full) mask_tail(s_nxt, (j + 1) * BC);  // tile j+1 is the ragged one
+      if (!STEADY && needs_mask(j + 1)) mask_tail(s_nxt, (j + 1) * BC);
       advance_max(s_nxt);
+    }
+    if (wg_next) {
       if (copies)
         vm_wait<2 * kPer>();
       else
@@ -363,15 +397,17 @@ void flash_fwd_half(FwdParams p) {
   using T = std::true_type;
   using F = std::false_type;
   int j = 0;
-  // steady groups: every step's copies exist (j + 3 + 3 < n_tiles) and the
-  // tile after the group's last one is full (j + 4 < n_full)
-  for (; j + 6 < n_tiles && j + 4 < n_full; j += 4) {
+  // steady groups: every step's copies exist (j + 3 + 3 < kt_end), the tile
+  // after the group's last one is full (j + 4 < n_full) and (causal) lies
+  // below every wave's diagonal (j + 4 < qt * BR / BC, wave 0's diagonal)
+  const int steady_end = CAUSAL ? min(n_full, qt * (BR / BC)) : n_full;
+  for (; j + 6 < kt_end && j + 4 < steady_end; j += 4) {
     step(j, sa, sb, std::integral_constant<int, 0>{}, T{});
     step(j + 1, sb, sa, std::integral_constant<int, 1>{}, T{});
     step(j + 2, sa, sb, std::integral_constant<int, 2>{}, T{});
     step(j + 3, sb, sa, std::integral_constant<int, 3>{}, T{});
   }
-  for (; j < n_tiles; ++j) {
+  for (; j < kt_end; ++j) {
     step(j, sa, sb, std::integral_constant<int, 0>{}, F{});
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) sa[qb] = sb[qb];
@@ -404,7 +440,7 @@ void flash_fwd_half(FwdParams p) {
 // (32x32x2: lane l supplies A[l%32][l/32] and B[l/32][l%32], one element each;
 // the accumulator layout is that of the half-precision product).
 // ---------------------------------------------------------------------------
-template <int D, int NW>
+template <int D, int NW, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64) void flash_fwd_f32(FwdParams p) {
   constexpr int NT = NW * 64, BR = NW * 32;
   constexpr int BC = 32;
@@ -416,7 +452,8 @@ __global__ __launch_bounds__(NW * 64) void flash_fwd_f32(FwdParams p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, g = lane >> 5;
   const int blk = xcd_remap(blockIdx.x, p.n_blocks);
-  const int bh = blk / p.n_qtiles, qt = blk % p.n_qtiles;
+  const int bh = blk / p.n_qtiles;
+  const int qt = CAUSAL ? p.n_qtiles - 1 - blk % p.n_qtiles : blk % p.n_qtiles;
   const int N = p.n;
   const int64_t head = (int64_t)bh * N * D * 4;
   const char* Q = p.q + head;
@@ -437,6 +474,12 @@ __global__ __launch_bounds__(NW * 64) void flash_fwd_f32(FwdParams p) {
   for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
   const int n_tiles = (N + BC - 1) / BC;
+  const int n_full = N / BC;
+  // key tiles of this workgroup and of this wave (see flash_fwd_half)
+  const int kt_end = CAUSAL ? min(n_tiles, (qt + 1) * (BR / BC)) : n_tiles;
+  const int diag = CAUSAL ? (qt * BR + wave * 32) / BC : n_tiles;
+  const int my_last = min(diag, n_tiles - 1);
+  const int key_lim = CAUSAL ? min(q_row, N - 1) : N - 1;
 
   KS ks;
   VS vs;
@@ -448,53 +491,56 @@ __global__ __launch_bounds__(NW * 64) void flash_fwd_f32(FwdParams p) {
   __syncthreads();
 
   auto step = [&](int j, auto mask_tag) {
-    constexpr bool MASK = decltype(mask_tag)::value;
+    constexpr bool MASK_ANY = decltype(mask_tag)::value;
+    const bool MASK = MASK_ANY && (j == n_full || (CAUSAL && j == diag));
     const char* kbuf = smem + (j & 1) * kStage;
     const char* vbuf = kbuf + KS::kBytes;
-    const bool more = j + 1 < n_tiles;
+    const bool more = j + 1 < kt_end;
     if (more) {
       ks.load(K, (j + 1) * BC, N, tid);
       vs.load(V, (j + 1) * BC, N, tid);
     }
 
-    f32x16 s[1] = {f32x16{}};
+    if (!CAUSAL || j <= my_last) {
+      f32x16 s[1] = {f32x16{}};
 #pragma unroll
-    for (int i = 0; i < D / 8; ++i) {
-      const f32x4 a = __builtin_bit_cast(f32x4, KS::read16(kbuf, l32, (i * 8 + g * 4) * 4));
+      for (int i = 0; i < D / 8; ++i) {
+        const f32x4 a = __builtin_bit_cast(f32x4, KS::read16(kbuf, l32, (i * 8 + g * 4) * 4));
 #pragma unroll
-      for (int e = 0; e < 4; ++e) s[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[e], qf[i][e], s[0], 0, 0, 0);
-    }
-
-    const int key0 = j * BC;
-    if constexpr (MASK) hide_tail(s, key0, N, g, c >= 0.f ? -INFINITY : INFINITY);
-
-    float alpha;
-    if (update_max(row_max_scaled(s, c), m_run, l_run, alpha)) {
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) acc[db] *= alpha;
-    }
-
-    float pr[16];
-    float lsum = 0.f;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float pv = exp2_fast(fmaf(s[0][r], c, -m_run));
-      if constexpr (MASK) {
-        if (key0 + score_key(0, r, g) >= N) pv = 0.f;
+        for (int e = 0; e < 4; ++e) s[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[e], qf[i][e], s[0], 0, 0, 0);
       }
-      pr[r] = pv;
-      lsum += pv;
-    }
-    l_run += lsum;
 
-    // O^T += V^T P^T, one product per score register: lane group g supplies
-    // key score_key(0, r, g) for both operands.
+      const int key0 = j * BC;
+      if (MASK) hide_after(s, key0, key_lim, g, c >= 0.f ? -INFINITY : INFINITY);
+
+      float alpha;
+      if (update_max(row_max_scaled(s, c), m_run, l_run, alpha)) {
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+        for (int db = 0; db < D / 32; ++db) acc[db] *= alpha;
+      }
+
+      float pr[16];
+      float lsum = 0.f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(
-            VS::read4(vbuf, score_key(0, r, g), (db * 32 + l32) * 4), pr[r], acc[db], 0, 0, 0);
+      for (int r = 0; r < 16; ++r) {
+        float pv = exp2_fast(fmaf(s[0][r], c, -m_run));
+        if (MASK) {
+          if (key0 + score_key(0, r, g) > key_lim) pv = 0.f;
+        }
+        pr[r] = pv;
+        lsum += pv;
+      }
+      l_run += lsum;
+
+      // O^T += V^T P^T, one product per score register: lane group g supplies
+      // key score_key(0, r, g) for both operands.
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(
+              VS::read4(vbuf, score_key(0, r, g), (db * 32 + l32) * 4), pr[r], acc[db], 0, 0, 0);
+    }
 
     if (more) {
       char* nbuf = smem + ((j + 1) & 1) * kStage;
@@ -503,9 +549,12 @@ __global__ __launch_bounds__(NW * 64) void flash_fwd_f32(FwdParams p) {
     }
     __syncthreads();
   };
-  const int n_full = N / BC;
-  for (int j = 0; j < n_full; ++j) step(j, std::false_type{});
-  if (n_full < n_tiles) step(n_full, std::true_type{});
+  if (CAUSAL) {
+    for (int j = 0; j < kt_end; ++j) step(j, std::true_type{});
+  } else {
+    for (int j = 0; j < n_full; ++j) step(j, std::false_type{});
+    if (n_full < n_tiles) step(n_full, std::true_type{});
+  }
 
   const float l_tot = pair_sum(l_run);
   const float inv = 1.f / l_tot;
@@ -528,7 +577,7 @@ constexpr int kWavesHalf = 4;
 constexpr int kQueryBlocksHalf = 1;
 constexpr int kWavesF32 = 4;
 
-template <class E, int D, int QB>
+template <class E, int D, int QB, bool CAUSAL>
 hipError_t run_half(const AttnArgs& a) {
   constexpr int BR = kWavesHalf * 32 * QB;
   FwdParams p;
@@ -542,15 +591,15 @@ hipError_t run_half(const AttnArgs& a) {
   p.n_blocks = a.B * a.H * p.n_qtiles;
   p.c = a.scale * kLog2e;
   if (a.scale < 0.f)
-    hipLaunchKernelGGL((flash_fwd_half<E, D, kWavesHalf, QB, true>), dim3(p.n_blocks), dim3(kWavesHalf * 64), 0,
-                       a.stream, p);
+    hipLaunchKernelGGL((flash_fwd_half<E, D, kWavesHalf, QB, true, CAUSAL>), dim3(p.n_blocks),
+                       dim3(kWavesHalf * 64), 0, a.stream, p);
   else
-    hipLaunchKernelGGL((flash_fwd_half<E, D, kWavesHalf, QB, false>), dim3(p.n_blocks), dim3(kWavesHalf * 64), 0,
-                       a.stream, p);
+    hipLaunchKernelGGL((flash_fwd_half<E, D, kWavesHalf, QB, false, CAUSAL>), dim3(p.n_blocks),
+                       dim3(kWavesHalf * 64), 0, a.stream, p);
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, bool CAUSAL>
 hipError_t run_f32(const AttnArgs& a) {
   constexpr int BR = kWavesF32 * 32;
   FwdParams p;
@@ -563,7 +612,7 @@ hipError_t run_f32(const AttnArgs& a) {
   p.n_qtiles = (a.N + BR - 1) / BR;
   p.n_blocks = a.B * a.H * p.n_qtiles;
   p.c = a.scale * kLog2e;
-  hipLaunchKernelGGL((flash_fwd_f32<D, kWavesF32>), dim3(p.n_blocks), dim3(kWavesF32 * 64), 0, a.stream, p);
+  hipLaunchKernelGGL((flash_fwd_f32<D, kWavesF32, CAUSAL>), dim3(p.n_blocks), dim3(kWavesF32 * 64), 0, a.stream, p);
   return hipGetLastError();
 }
 
@@ -571,15 +620,20 @@ hipError_t run_f32(const AttnArgs& a) {
 
 int flash_rows_per_block(int dtype, int /*d*/) { return dtype == kF32 ? kWavesF32 * 32 : kWavesHalf * 32 * kQueryBlocksHalf; }
 
-hipError_t launch_flash(const AttnArgs& a) {
+template <bool CAUSAL>
+hipError_t launch(const AttnArgs& a) {
+  constexpr int QB = kQueryBlocksHalf;
   switch (a.dtype) {
     case kBF16:
-      return a.d == 128 ? run_half<BF16, 128, kQueryBlocksHalf>(a) : run_half<BF16, 64, kQueryBlocksHalf>(a);
+      return a.d == 128 ? run_half<BF16, 128, QB, CAUSAL>(a) : run_half<BF16, 64, QB, CAUSAL>(a);
     case kF16:
-      return a.d == 128 ? run_half<F16, 128, kQueryBlocksHalf>(a) : run_half<F16, 64, kQueryBlocksHalf>(a);
+      return a.d == 128 ? run_half<F16, 128, QB, CAUSAL>(a) : run_half<F16, 64, QB, CAUSAL>(a);
     default:
-      return a.d == 128 ? run_f32<128>(a) : run_f32<64>(a);
+      return a.d == 128 ? run_f32<128, CAUSAL>(a) : run_f32<64, CAUSAL>(a);
   }
 }
+
+hipError_t launch_flash(const AttnArgs& a) { return launch<false>(a); }
+hipError_t launch_flash_causal(const AttnArgs& a) { return launch<true>(a); }
 
 }  // namespace fa

@@ -61,6 +61,10 @@ def call(L, q=P, k=P2, v=P3, o=PO, lse=PL, B=1, H=1, N=16, d=64, scale=0.125, dt
     return L.flash_attn_fwd(q, k, v, o, lse, B, H, N, d, scale, dtype, None)
 
 
+def call_causal(L, q=P, k=P2, v=P3, o=PO, lse=PL, B=1, H=1, N=16, d=64, scale=0.125, dtype=2):
+    return L.flash_attn_fwd_causal(q, k, v, o, lse, B, H, N, d, scale, dtype, None)
+
+
 def naive(L, ws=0x60000, ws_bytes=1 << 20, **kw):
     args = dict(q=P, k=P2, v=P3, o=PO, lse=PL, B=1, H=1, N=16, d=64, scale=0.125, dtype=2)
     args.update(kw)
@@ -69,7 +73,7 @@ def naive(L, ws=0x60000, ws_bytes=1 << 20, **kw):
                             a["scale"], a["dtype"], ws, ws_bytes, None)
 
 
-@pytest.mark.parametrize("entry", [call, naive])
+@pytest.mark.parametrize("entry", [call, call_causal, naive])
 def test_validation_errors(L, entry):
     assert entry(L, B=-1) == fa.FA_ERR_SHAPE
     assert entry(L, N=-5) == fa.FA_ERR_SHAPE
@@ -89,7 +93,7 @@ def test_validation_errors(L, entry):
     assert entry(L, B=1 << 20, H=1 << 10, N=1 << 20) == fa.FA_ERR_SHAPE
 
 
-@pytest.mark.parametrize("entry", [call, naive])
+@pytest.mark.parametrize("entry", [call, call_causal, naive])
 def test_empty_problems_are_noops(L, entry):
     # nothing is launched and pointers are not looked at
     assert entry(L, B=0, q=None, k=None, v=None, o=None, lse=None) == fa.FA_OK

@@ -230,3 +230,92 @@ def test_unsupported_head_size_raises():
     with pytest.raises(fa.FlashAttnError) as e:
         fa.flash_attn_fwd(x, x, x)
     assert e.value.status == fa.FA_ERR_UNSUPPORTED
+
+
+# -- causal (prefill) attention: query i sees keys 0..i --------------------------
+
+def causal_rows_reference(q, k, v, scale, rows):
+    """Oracle rows of causal attention: row i is attention of query i over the
+    prefix of keys 0..i (the definition, evaluated row by row)."""
+    lead = q.shape[:-2]
+    o = np.empty(lead + (len(rows), v.shape[-1]))
+    lse = np.empty(lead + (len(rows),))
+    for t, i in enumerate(rows):
+        oi, li = attention_reference(q[..., i:i + 1, :], k[..., :i + 1, :], v[..., :i + 1, :], scale)
+        o[..., t, :] = oi[..., 0, :]
+        lse[..., t] = li[..., 0]
+    return o, lse
+
+
+def run_causal(q, k, v, dtype, scale):
+    return run(lambda *a: fa.flash_attn_fwd(*a, causal=True), q, k, v, dtype, scale)
+
+
+@pytest.mark.parametrize("name", ["n256_d64_fp32", "n4096_d128_bf16", "n10000_d128_fp16", "b32_n512_d64_bf16"])
+def test_causal_workload(name):
+    w = WORKLOADS[name]
+    print(f"[parity] causal {name}", flush=True)
+    q, k, v = make_inputs(w)
+    o, lse = run_causal(q, k, v, w.dtype, w.scale)
+    if w.N <= 4096:
+        o_ref, lse_ref = attention_reference(q, k, v, w.scale, causal=True)
+        assert_close(o, lse, o_ref, lse_ref, w.dtype, f"causal {name}")
+    else:  # 10000 tokens: sampled rows, the diagonal tiles of every query tile included
+        rows = np.unique(np.concatenate([sample_rows(w.N, 48), np.arange(0, w.N, 128), [w.N - 16, w.N - 1]]))
+        o_ref, lse_ref = causal_rows_reference(q, k, v, w.scale, rows)
+        assert_close(o[:, :, rows], lse[:, :, rows], o_ref, lse_ref, w.dtype, f"causal {name} sampled")
+
+
+def test_causal_long_context_sampled_rows(long_context):
+    """Full-size 32K workload with causal masking, 40 sampled rows per head."""
+    w, (q, k, v), (tq, tk, tv) = long_context
+    print("[parity] causal n32768_d128_bf16 sampled rows", flush=True)
+    o, lse = fa.flash_attn_fwd(tq, tk, tv, w.scale, causal=True)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([sample_rows(w.N, 36), [31, 32, 127, 128]]))
+    o_s = o[:, :, rows].float().cpu().numpy().astype(np.float64)
+    lse_s = lse[:, :, rows].cpu().numpy().astype(np.float64)
+    o_ref, lse_ref = causal_rows_reference(q, k, v, w.scale, rows)
+    assert_close(o_s, lse_s, o_ref, lse_ref, w.dtype, "causal n32768 sampled")
+    # row 0 sees key 0 alone: O_0 is v_0 exactly
+    assert torch.equal(o[:, :, 0], tv[:, :, 0])
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "fp16", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("n", EDGE_N + [300, 1000])
+def test_causal_edge_shapes(n, d, dtype):
+    w = Workload("cedge", 2, 3, n, d, dtype, 2000 + n + d)
+    q, k, v = make_inputs(w)
+    o, lse = run_causal(q, k, v, dtype, w.scale)
+    o_ref, lse_ref = attention_reference(q, k, v, w.scale, causal=True)
+    assert_close(o, lse, o_ref, lse_ref, dtype, f"causal n={n} d={d} {dtype}")
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.09, 4.0])
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_causal_scale_values(scale, dtype):
+    """Zero (prefix means), negative and very large scales."""
+    w = Workload("cscales", 1, 2, 389, 64, dtype, 16)
+    q, k, v = make_inputs(w)
+    o, lse = run_causal(q, k, v, dtype, scale)
+    o_ref, lse_ref = attention_reference(q, k, v, scale, causal=True)
+    assert_close(o, lse, o_ref, lse_ref, dtype, f"causal scale={scale}", tol=max_abs_tol(dtype, scale, w.d))
+
+
+def test_causal_deterministic_and_independent_of_future():
+    """Bitwise run-to-run determinism, and rows before a perturbed token are
+    bitwise unchanged (nothing after row i reaches row i)."""
+    w = Workload("cdet", 1, 2, 2000, 128, "bf16", 17)
+    q, k, v = make_inputs(w)
+    tq, tk, tv = dev(q, w.dtype), dev(k, w.dtype), dev(v, w.dtype)
+    o1, l1 = fa.flash_attn_fwd(tq, tk, tv, causal=True)
+    o2, l2 = fa.flash_attn_fwd(tq, tk, tv, causal=True)
+    tk2, tv2 = tk.clone(), tv.clone()
+    tk2[:, :, 1500:] *= 3.0
+    tv2[:, :, 1500:] -= 1.0
+    o3, l3 = fa.flash_attn_fwd(tq, tk2, tv2, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    assert torch.equal(o1[:, :, :1500], o3[:, :, :1500]) and torch.equal(l1[:, :, :1500], l3[:, :, :1500])
+    assert not torch.equal(o1[:, :, 1500:], o3[:, :, 1500:])
