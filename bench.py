@@ -142,6 +142,9 @@ def traffic_sweep(entry: str) -> None:
         shape = (1, 16, n, 128)
         q, k, v = (torch.randn(shape, generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
                    for _ in range(3))
+        torch.cuda.synchronize(dev)
+        torch.cuda.reset_peak_memory_stats(dev)
+        base = torch.cuda.memory_allocated(dev)
         o = torch.empty_like(q)
         ws = None
         if entry == "naive":
@@ -157,9 +160,77 @@ def traffic_sweep(entry: str) -> None:
             torch.cuda.synchronize(dev)
             times.append(time.perf_counter() - t0)
         print(json.dumps({"sweep": entry, "N": n, "B": 1, "H": 16, "d": 128, "dtype": "bf16",
-                          "wall_ms": round(times[-1] * 1e3, 4)}), flush=True)
+                          "wall_ms": round(times[-1] * 1e3, 4),
+                          "extra_device_bytes": int(torch.cuda.max_memory_allocated(dev) - base)}), flush=True)
         del q, k, v, o, ws
         torch.cuda.empty_cache()
+
+
+CROSSOVER_N = (16, 32, 64, 128, 256, 512, 1024, 2048, 4096)
+
+
+def crossover_sweep(reps: int = 10) -> None:
+    """Fused versus three-pass path at a fixed amount of work: H = 16, d = 128,
+    bf16, B chosen so that B*H*N^2 = 16*4096^2 at every N. For each N and path:
+    median kernel time over `reps` launches (HIP events on the current stream,
+    after 2 warm-ups) and the device memory the call needs beyond Q, K, V
+    (the outputs, plus the three-pass workspace), from torch's allocator peak.
+    One JSON line per (path, N); a final line names the crossover, the largest
+    N at which the three-pass path is faster (null if it never is)."""
+    import numpy as np
+    import torch
+
+    import io_aware_tiled_06_amd as fa
+
+    if not os.path.exists(fa.LIB_PATH):
+        import __graft_entry__
+
+        __graft_entry__.build()
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev).manual_seed(6)
+    work = 16 * 4096 * 4096
+    faster_naive = []
+    for n in CROSSOVER_N:
+        b = max(1, work // (16 * n * n))
+        shape = (b, 16, n, 128)
+        q, k, v = (torch.randn(shape, generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+                   for _ in range(3))
+        ms = {}
+        for entry in ("flash", "naive"):
+            torch.cuda.synchronize(dev)
+            torch.cuda.reset_peak_memory_stats(dev)
+            base = torch.cuda.memory_allocated(dev)
+            o = torch.empty_like(q)
+            lse = torch.empty((b, 16, n), dtype=torch.float32, device=dev)
+            ws = None
+            if entry == "naive":
+                ws = torch.empty(fa.attn_naive_workspace_bytes(b, 16, n, "bf16"), dtype=torch.uint8, device=dev)
+            call = (lambda: fa.attn_naive_fwd(q, k, v, out=o, workspace=ws)) if entry == "naive" else \
+                (lambda: fa.flash_attn_fwd(q, k, v, out=o))
+            for _ in range(2):
+                call()
+            st = torch.cuda.current_stream(dev)
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+            ev[0].record(st)
+            for i in range(reps):
+                call()
+                ev[i + 1].record(st)
+            torch.cuda.synchronize(dev)
+            t = float(np.median([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]))
+            extra = torch.cuda.max_memory_allocated(dev) - base
+            ms[entry] = t
+            print(json.dumps({"crossover": entry, "N": n, "B": b, "H": 16, "d": 128, "dtype": "bf16",
+                              "kernel_ms": round(t, 5),
+                              "tflops": round(4.0 * b * 16 * n * n * 128 / (t * 1e-3) / 1e12, 2),
+                              "extra_device_bytes": int(extra)}), flush=True)
+            del o, lse, ws
+            torch.cuda.empty_cache()
+        if ms["naive"] < ms["flash"]:
+            faster_naive.append(n)
+        del q, k, v
+        torch.cuda.empty_cache()
+    print(json.dumps({"crossover_naive_faster_up_to_N": max(faster_naive) if faster_naive else None,
+                      "naive_faster_at": faster_naive}), flush=True)
 
 
 def main() -> int:
@@ -176,12 +247,17 @@ def main() -> int:
                     help="only run a plain device copy of BYTES (counter calibration) and exit")
     ap.add_argument("--traffic-sweep", choices=["flash", "naive"], default=None,
                     help="only run the N sweep used for the traffic-versus-N counters and exit")
+    ap.add_argument("--crossover-sweep", action="store_true",
+                    help="only run the fused-versus-three-pass sweep at fixed work (time and memory) and exit")
     args = ap.parse_args()
     if args.copy_calibration:
         copy_calibration(args.copy_calibration, 3)
         return 0
     if args.traffic_sweep:
         traffic_sweep(args.traffic_sweep)
+        return 0
+    if args.crossover_sweep:
+        crossover_sweep()
         return 0
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path",
