@@ -184,3 +184,48 @@ def attention_online(q, k, v, scale: float, block: int, causal: bool = False):
         out[idx] = acc / l[:, None]
         lse[idx] = m + np.log(l)
     return out, lse
+
+
+def attention_backward_reference(q, k, v, do, scale: float, causal: bool = False):
+    """Gradients of attention by the chain rule applied to its definition, float64.
+
+    With S = scale * q k^T, P = softmax_rows(S) (causal: over keys j <= i),
+    O = P v and an upstream gradient dO = dL/dO:
+        dV     = P^T dO
+        dP     = dO v^T
+        D_i    = sum_j P_ij dP_ij            (= dO_i . O_i)
+        dS     = P * (dP - D)                (softmax Jacobian, row by row)
+        dQ     = scale * dS k
+        dK     = scale * dS^T q
+    The pages stop at the forward pass; "What FlashAttention actually buys",
+    "Why the distinction matters downstream", mentions that the backward pass
+    recomputes the score tiles instead of storing them -- the kernels do that,
+    using the forward's LSE; this reference materialises P per head.
+
+    q, k [..., N, d], v, do [..., N, dv]. Returns (dQ, dK, dV), float64.
+    """
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    _check(q, k, v)
+    if do.shape != q.shape[:-1] + (v.shape[-1],):
+        raise ValueError("do must have the shape of the output")
+    nq, nk = q.shape[-2], k.shape[-2]
+    if causal and nq != nk:
+        raise ValueError("causal attention needs as many queries as keys")
+    s = np.float64(scale)
+    dq = np.empty_like(q)
+    dk = np.empty_like(k)
+    dv = np.empty_like(v)
+    for idx in np.ndindex(*q.shape[:-2]):
+        qh, kh, vh, doh = q[idx], k[idx], v[idx], do[idx]
+        scores = s * (qh @ kh.T)
+        if causal:
+            scores[_future(0, nq, nk)] = -np.inf
+        e = np.exp(scores - scores.max(axis=1, keepdims=True))
+        p = e / e.sum(axis=1, keepdims=True)
+        dv[idx] = p.T @ doh
+        dp = doh @ vh.T
+        delta = (p * dp).sum(axis=1, keepdims=True)
+        ds = p * (dp - delta)
+        dq[idx] = s * (ds @ kh)
+        dk[idx] = s * (ds.T @ qh)
+    return dq, dk, dv

@@ -363,3 +363,123 @@ def failing_pins(fn, pins=None):
         except Exception:  # noqa: BLE001 - any failure counts
             bad.append(pin.__name__)
     return bad
+
+
+# ---------------------------------------------------------------------------
+# Backward pass: each pin takes bwd(q, k, v, do, scale, causal) -> (dQ, dK, dV).
+# ---------------------------------------------------------------------------
+
+
+def _forward_loss(q, k, v, do, scale, causal):
+    """L = sum(O * dO), with O from the (separately pinned) forward oracle."""
+    from oracle import attention_reference
+
+    o, _ = attention_reference(q, k, v, scale, causal=causal)
+    return float(np.sum(o * do))
+
+
+def pin_bwd_finite_differences(bwd, tol=2e-8):
+    """Every gradient entry against a central difference of L = sum(O * dO)."""
+    for causal in (False, True):
+        rng = _rng(400 + causal)
+        n, d = 5, 3
+        q, k, v, do = (rng.standard_normal((1, n, d)) for _ in range(4))
+        scale = 0.7
+        grads = bwd(q, k, v, do, scale, causal)
+        h = 1e-5
+        for which, x in enumerate((q, k, v)):
+            for idx in np.ndindex(*x.shape):
+                xp, xm = x.copy(), x.copy()
+                xp[idx] += h
+                xm[idx] -= h
+                args_p = [q, k, v]
+                args_m = [q, k, v]
+                args_p[which], args_m[which] = xp, xm
+                fd = (_forward_loss(*args_p, do, scale, causal) - _forward_loss(*args_m, do, scale, causal)) / (2 * h)
+                assert abs(grads[which][idx] - fd) <= tol * max(1.0, abs(fd)), (causal, which, idx, grads[which][idx], fd)
+
+
+def pin_bwd_library(bwd):
+    """torch's float64 autograd through its own CPU attention (causal too)."""
+    import torch
+    import torch.nn.functional as F
+
+    rng = _rng(401)
+    for causal in (False, True):
+        for (b, h, n, d) in ((1, 2, 33, 8), (2, 1, 70, 16)):
+            q, k, v, do = (rng.standard_normal((b, h, n, d)) for _ in range(4))
+            scale = 1.0 / math.sqrt(d)
+            dq, dk, dv = bwd(q, k, v, do, scale, causal)
+            tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+            o = F.scaled_dot_product_attention(tq, tk, tv, scale=scale, is_causal=causal)
+            o.backward(torch.from_numpy(do))
+            for mine, ref in ((dq, tq.grad), (dk, tk.grad), (dv, tv.grad)):
+                assert np.max(np.abs(mine - ref.numpy())) <= 1e-12, (causal, b, h, n, d)
+
+
+def pin_bwd_single_key(bwd):
+    """N = 1: O = v_0 whatever q, k, so dV = dO and dQ = dK = 0."""
+    rng = _rng(402)
+    q, k, v, do = (rng.standard_normal((2, 1, 7)) for _ in range(4))
+    dq, dk, dv = bwd(q, k, v, do, 0.8, False)
+    assert np.max(np.abs(dv - do)) <= 1e-15
+    assert np.max(np.abs(dq)) <= 1e-15 and np.max(np.abs(dk)) <= 1e-15
+
+
+def pin_bwd_zero_scale(bwd):
+    """scale = 0: uniform weights, so dQ = dK = 0 and dV_j = mean_i dO_i
+    (causal: dV_j = sum over i >= j of dO_i / (i + 1))."""
+    rng = _rng(403)
+    n = 20
+    q, k, v, do = (rng.standard_normal((1, n, 6)) for _ in range(4))
+    dq, dk, dv = bwd(q, k, v, do, 0.0, False)
+    assert np.max(np.abs(dq)) <= 1e-15 and np.max(np.abs(dk)) <= 1e-15
+    assert np.max(np.abs(dv - do.mean(axis=1, keepdims=True))) <= 1e-14
+    dq, dk, dv = bwd(q, k, v, do, 0.0, True)
+    expect = np.stack([sum(do[0, i] / (i + 1) for i in range(j, n)) for j in range(n)])[None]
+    assert np.max(np.abs(dq)) <= 1e-15 and np.max(np.abs(dk)) <= 1e-15
+    assert np.max(np.abs(dv - expect)) <= 1e-14
+
+
+def pin_bwd_linear_in_upstream(bwd):
+    """Gradients are linear in dO."""
+    rng = _rng(404)
+    q, k, v, d1, d2 = (rng.standard_normal((2, 25, 8)) for _ in range(5))
+    for causal in (False, True):
+        a = bwd(q, k, v, d1, 0.4, causal)
+        b = bwd(q, k, v, d2, 0.4, causal)
+        c = bwd(q, k, v, 2.0 * d1 - 3.0 * d2, 0.4, causal)
+        for x, y, z in zip(a, b, c):
+            assert np.max(np.abs(z - (2.0 * x - 3.0 * y))) <= 1e-12
+
+
+def pin_bwd_key_shift(bwd):
+    """Adding one vector to every key moves each row's scores by a constant, so
+    the output does not change: the key gradients sum to zero over the keys."""
+    rng = _rng(405)
+    q, k, v, do = (2.0 * rng.standard_normal((2, 40, 8)) for _ in range(4))
+    for causal in (False, True):
+        _, dk, _ = bwd(q, k, v, do, 0.5, causal)
+        assert np.max(np.abs(dk.sum(axis=1))) <= 1e-12 * max(1.0, np.max(np.abs(dk)))
+
+
+def pin_bwd_causal_future(bwd):
+    """Causal: with dO zero after position t, keys and values after t get no
+    gradient (no query that sees them has an upstream gradient)."""
+    rng = _rng(406)
+    q, k, v, do = (rng.standard_normal((1, 30, 8)) for _ in range(4))
+    do[:, 18:] = 0.0
+    _, dk, dv = bwd(q, k, v, do, 0.6, True)
+    assert np.max(np.abs(dk[:, 18:])) == 0.0 and np.max(np.abs(dv[:, 18:])) == 0.0
+    assert np.max(np.abs(dv[:, :18])) > 0.0
+
+
+BWD_PINS = [
+    pin_bwd_finite_differences,
+    pin_bwd_library,
+    pin_bwd_single_key,
+    pin_bwd_zero_scale,
+    pin_bwd_linear_in_upstream,
+    pin_bwd_key_shift,
+    pin_bwd_causal_future,
+]

@@ -162,3 +162,42 @@ def test_causal_mutant_harness_is_sound():
         return (e / l) @ v, (m + np.log(l))[..., 0]
 
     assert failing_pins(correct, CAUSAL_PINS) == []
+
+
+# -- backward-pass mistakes ------------------------------------------------------
+
+from pins import BWD_PINS  # noqa: E402
+
+BWD_MUTATIONS = ["dq_no_scale", "no_delta", "delta_wrong_axis", "dk_untransposed", "dv_untransposed",
+                 "ds_sign", "dq_uses_v", "causal_mask_dropped"]
+
+
+def _bwd_mutant(q, k, v, do, scale, causal, mutation):
+    q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
+    s = float(scale)
+    out = [np.empty_like(q), np.empty_like(k), np.empty_like(v)]
+    n = q.shape[-2]
+    for idx in np.ndindex(*q.shape[:-2]):
+        qh, kh, vh, doh = q[idx], k[idx], v[idx], do[idx]
+        scores = s * (qh @ kh.T)
+        if causal and mutation != "causal_mask_dropped":
+            scores = np.where(np.arange(n)[None, :] > np.arange(n)[:, None], -np.inf, scores)
+        e = np.exp(scores - scores.max(axis=1, keepdims=True))
+        p = e / e.sum(axis=1, keepdims=True)
+        dv = p @ doh if mutation == "dv_untransposed" else p.T @ doh
+        dp = doh @ vh.T
+        axis = 0 if mutation == "delta_wrong_axis" else 1
+        delta = 0.0 if mutation == "no_delta" else (p * dp).sum(axis=axis, keepdims=True)
+        ds = p * (dp - delta)
+        if mutation == "ds_sign":
+            ds = -ds
+        dq = (1.0 if mutation == "dq_no_scale" else s) * (ds @ (vh if mutation == "dq_uses_v" else kh))
+        dk = s * (ds @ qh if mutation == "dk_untransposed" else ds.T @ qh)
+        out[0][idx], out[1][idx], out[2][idx] = dq, dk, dv
+    return tuple(out)
+
+
+@pytest.mark.parametrize("mutation", BWD_MUTATIONS)
+def test_backward_mutant_is_caught(mutation):
+    bad = failing_pins(lambda *a: _bwd_mutant(*a, mutation), BWD_PINS)
+    assert bad, f"backward mutation {mutation} passed every backward pin"

@@ -136,3 +136,14 @@ def test_causal_needs_square():
     k = np.zeros((1, 5, 4))
     with pytest.raises(ValueError):
         attention_reference(q, k, k, 1.0, causal=True)
+
+
+# -- backward pass ---------------------------------------------------------------
+
+from oracle import attention_backward_reference  # noqa: E402
+from pins import BWD_PINS  # noqa: E402
+
+
+@pytest.mark.parametrize("pin", BWD_PINS, ids=lambda p: p.__name__)
+def test_backward_reference_meets_pin(pin):
+    pin(lambda q, k, v, do, s, causal: attention_backward_reference(q, k, v, do, s, causal=causal))
