@@ -233,6 +233,14 @@ def crossover_sweep(reps: int = 10) -> None:
                       "naive_faster_at": faster_naive}), flush=True)
 
 
+def bwd_compulsory_bytes(w) -> int:
+    """Bytes a backward pass must move at least: Q, K, V, O and dO read, dQ, dK
+    and dV written (element type), LSE read and the row statistic D written
+    then read (float32)."""
+    elems = w.B * w.H * w.N * w.d
+    return 8 * elems * w.elem_bytes + 3 * 4 * w.B * w.H * w.N
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -240,6 +248,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="n32768_d128_bf16")
     ap.add_argument("--entry", choices=["flash", "naive"], default="flash")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward pass (dQ, dK, dV from the forward's O and LSE); FLOPs counted as "
+                         "2.5x the forward's (the five N x N x d products of the gradient)")
     ap.add_argument("--causal", action="store_true",
                     help="time the causal entry point (query i sees keys 0..i); FLOPs count visible pairs only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -283,13 +294,21 @@ def main() -> int:
     tq, tk, tv = (torch.from_numpy(x).to(tdt).to(dev) for x in (q, k, v))
     o = torch.empty_like(tq)
     ws = None
-    if args.causal and args.entry != "flash":
-        print("--causal applies to the fused entry point only", file=sys.stderr)
+    if (args.causal or args.backward) and args.entry != "flash":
+        print("--causal and --backward apply to the fused entry points only", file=sys.stderr)
         return 2
     if args.entry == "naive":
         nbytes = fa.attn_naive_workspace_bytes(w.B, w.H, w.N, w.dtype)
         ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
         step = lambda: fa.attn_naive_fwd(tq, tk, tv, w.scale, out=o, workspace=ws)  # noqa: E731
+    elif args.backward:
+        o, lse = fa.flash_attn_fwd(tq, tk, tv, w.scale, causal=args.causal)
+        gen = torch.Generator(device=dev).manual_seed(w.seed + 100)
+        dout = torch.randn(tq.shape, generator=gen, device=dev, dtype=torch.float32).to(tdt)
+        grads = [torch.empty_like(tq) for _ in range(3)]
+        delta = torch.empty(lse.shape, dtype=torch.float32, device=dev)
+        step = lambda: fa.flash_attn_bwd(tq, tk, tv, o, lse, dout, w.scale, causal=args.causal,  # noqa: E731
+                                         dq=grads[0], dk=grads[1], dv=grads[2], delta=delta)
     else:
         step = lambda: fa.flash_attn_fwd(tq, tk, tv, w.scale, causal=args.causal, out=o)  # noqa: E731
 
@@ -314,12 +333,14 @@ def main() -> int:
     flops = traffic.attention_flops(w.B, w.H, w.N, w.d)
     if args.causal:  # visible (query, key) pairs: N (N + 1) / 2 per head
         flops = 2.0 * w.B * w.H * w.N * (w.N + 1) * w.d
+    if args.backward:
+        flops *= 2.5
     ms_per_step = wall / args.steps * 1e3
     value = flops / (ms_per_step * 1e-3) / 1e12
     kern_ms = float(np.mean(ev_ms))
     achieved = flops / (kern_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
-    hbm = None if args.causal else measured_traffic(w.name, args.entry)
+    hbm = None if (args.causal or args.backward) else measured_traffic(w.name, args.entry)
     line = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -333,7 +354,8 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic",
-        "config": {"workload": w.name, "entry": args.entry, "causal": bool(args.causal), "B": w.B, "H": w.H,
+        "config": {"workload": w.name, "entry": args.entry, "causal": bool(args.causal),
+                   "pass": "backward" if args.backward else "forward", "B": w.B, "H": w.H,
                    "N": w.N, "d": w.d,
                    "qk_sigma": w.qk_sigma, "seed": w.seed, "scale": w.scale},
         "pct_of_peak": round(100.0 * value / peak, 2),
@@ -346,11 +368,14 @@ def main() -> int:
             "traffic": hbm,
             "kernel_ms": round(kern_ms, 4),
             "kernel_ms_min": round(float(np.min(ev_ms)), 4),
-            "compulsory_bytes": traffic.compulsory_bytes(w.B, w.H, w.N, w.d, w.elem_bytes),
+            "compulsory_bytes": (bwd_compulsory_bytes(w) if args.backward
+                                 else traffic.compulsory_bytes(w.B, w.H, w.N, w.d, w.elem_bytes)),
         },
         "device": torch.cuda.get_device_name(dev),
     }
-    if not args.no_cpu_baseline:
+    if args.backward:
+        line["roofline"]["kernels"] = "bwd_delta + bwd_dq + bwd_dkdv (one backward pass)"
+    if not args.no_cpu_baseline and not args.backward:
         print("[bench] cpu baseline (float64 oracle)", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(w, q, k, v)
     print(json.dumps(line), flush=True)

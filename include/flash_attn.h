@@ -96,6 +96,39 @@ int flash_attn_fwd_causal(const void* q, const void* k, const void* v, void* o, 
                           int B, int H, int N, int d, float scale, int dtype, void* stream);
 
 /*
+ * flash_attn_bwd -- gradients of flash_attn_fwd: given the forward's inputs
+ * q, k, v, its outputs o and lse, and the upstream gradient dout = dL/dO,
+ * writes dq = dL/dQ, dk = dL/dK, dv = dL/dV. With P = exp(scale Q K^T - LSE):
+ *   dV = P^T dO,  dS = P * (dO V^T - D),  D_i = dO_i . O_i,
+ *   dQ = scale dS K,  dK = scale dS^T Q.
+ * The score tiles are recomputed from lse rather than stored ("What
+ * FlashAttention actually buys", "Why the distinction matters downstream"):
+ * nothing N x N is written.
+ *
+ * Arguments: q, k, v, o, dout, dq, dk, dv: [B,H,N,d] device pointers of
+ * `dtype` (FA_F16 or FA_BF16; FA_F32 returns FA_ERR_UNSUPPORTED); lse: the
+ * [B,H,N] float32 output of the forward pass with the same inputs and scale;
+ * delta: caller-owned [B,H,N] float32 scratch, overwritten with D (the
+ * library allocates nothing). All 16-byte aligned; outputs must not alias
+ * inputs. Three kernels run in order on `stream`. Arithmetic: products on the
+ * matrix cores with float32 accumulation, P and dS rounded to the input type
+ * before their products, gradients rounded to nearest even. Deterministic
+ * (no atomics). Validation and status codes as flash_attn_fwd (d in {64,128}).
+ */
+int flash_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                   const float* lse, void* dq, void* dk, void* dv, float* delta,
+                   int B, int H, int N, int d, float scale, int dtype, void* stream);
+
+/*
+ * flash_attn_bwd_causal -- the gradients of flash_attn_fwd_causal (query i
+ * attends keys 0..i); lse must come from flash_attn_fwd_causal. Arguments as
+ * flash_attn_bwd.
+ */
+int flash_attn_bwd_causal(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                          const float* lse, void* dq, void* dk, void* dv, float* delta,
+                          int B, int H, int N, int d, float scale, int dtype, void* stream);
+
+/*
  * attn_naive_workspace_bytes -- workspace for attn_naive_fwd to process every
  * head in one pass: B*H*N*N*(4 + e) bytes, e = element size of dtype (S is
  * held in float32, P in the input type). Any workspace of at least one head,

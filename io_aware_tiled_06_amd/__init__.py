@@ -17,6 +17,7 @@ import os
 __all__ = [
     "FlashAttnError",
     "flash_attn_fwd",
+    "flash_attn_bwd",
     "attn_naive_fwd",
     "attn_naive_workspace_bytes",
     "lib",
@@ -34,8 +35,8 @@ __all__ = [
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libflashattn.so")
-EXPORTED_SYMBOLS = ("flash_attn_fwd", "flash_attn_fwd_causal", "attn_naive_workspace_bytes", "attn_naive_fwd",
-                    "fa_strerror")
+EXPORTED_SYMBOLS = ("flash_attn_fwd", "flash_attn_fwd_causal", "flash_attn_bwd", "flash_attn_bwd_causal",
+                    "attn_naive_workspace_bytes", "attn_naive_fwd", "fa_strerror")
 
 # fa_status values (include/flash_attn.h)
 FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED = 0, 1, 2, 3
@@ -67,6 +68,10 @@ def lib() -> ctypes.CDLL:
         L.flash_attn_fwd.restype = i
         L.flash_attn_fwd_causal.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
         L.flash_attn_fwd_causal.restype = i
+        for name in ("flash_attn_bwd", "flash_attn_bwd_causal"):
+            fn = getattr(L, name)
+            fn.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
+            fn.restype = i
         L.attn_naive_workspace_bytes.argtypes = [i, i, i, i]
         L.attn_naive_workspace_bytes.restype = sz
         L.attn_naive_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, sz, vp]
@@ -158,6 +163,43 @@ def flash_attn_fwd(q, k, v, scale=None, *, causal=False, out=None, return_lse=Tr
     if st != FA_OK:
         raise FlashAttnError(st, "flash_attn_fwd_causal" if causal else "flash_attn_fwd")
     return o, lse
+
+
+def flash_attn_bwd(q, k, v, o, lse, dout, scale=None, *, causal=False, dq=None, dk=None, dv=None, delta=None,
+                   stream=None):
+    """Gradients of the fused forward pass (dQ, dK, dV) on the GPU.
+
+    q, k, v, o, dout: contiguous [B, H, N, d] float16/bfloat16 tensors on one
+    GPU; lse: the float32 [B, H, N] LSE that flash_attn_fwd returned for these
+    inputs (and the same `causal`). dq, dk, dv default to new tensors like q;
+    delta (float32 [B, H, N] scratch) to a new tensor. Returns (dq, dk, dv).
+    """
+    import torch
+
+    _check_inputs(q, k, v)
+    for name, t in (("o", o), ("dout", dout)):
+        if t.shape != q.shape or t.dtype != q.dtype or t.device != q.device or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous tensor of q's shape, dtype and device")
+    B, H, N, d = q.shape
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or lse.device != q.device or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor on q's device")
+    s = _default_scale(d) if scale is None else float(scale)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        if t.shape != q.shape or t.dtype != q.dtype or t.device != q.device or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous tensor of q's shape, dtype and device")
+    if delta is None:
+        delta = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    fn = lib().flash_attn_bwd_causal if causal else lib().flash_attn_bwd
+    with torch.cuda.device(q.device):
+        st = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+                dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), B, H, N, d, s, _dtype_code(q),
+                _stream_ptr(q, stream))
+    if st != FA_OK:
+        raise FlashAttnError(st, "flash_attn_bwd_causal" if causal else "flash_attn_bwd")
+    return dq, dk, dv
 
 
 def attn_naive_workspace_bytes(B: int, H: int, N: int, dtype: str) -> int:

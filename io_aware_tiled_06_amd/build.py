@@ -23,7 +23,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB_NAME = "libflashattn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = ["api.hip", "flash_fwd.hip", "naive.hip"]
+SOURCES = ["api.hip", "flash_fwd.hip", "flash_bwd.hip", "naive.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

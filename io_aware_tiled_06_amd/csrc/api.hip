@@ -81,6 +81,50 @@ int flash_attn_fwd_causal(const void* q, const void* k, const void* v, void* o, 
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+static int flash_attn_bwd_impl(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                               const float* lse, void* dq, void* dk, void* dv, float* delta, int B, int H, int N,
+                               int d, float scale, int dtype, void* stream, bool causal) {
+  bool empty;
+  const int st = validate(q, k, v, dq, lse, B, H, N, d, scale, dtype, &empty);
+  if (st != FA_OK || empty) return st;
+  if (dtype == FA_F32) return FA_ERR_UNSUPPORTED;
+  if (!o || !dout || !lse || !dk || !dv || !delta) return FA_ERR_NULL;
+  if (!aligned16(o) || !aligned16(dout) || !aligned16(dk) || !aligned16(dv) || !aligned16(delta))
+    return FA_ERR_ALIGN;
+  fa::BwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.dout = dout;
+  a.lse = lse;
+  a.delta = delta;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.B = B;
+  a.H = H;
+  a.N = N;
+  a.d = d;
+  a.scale = scale;
+  a.dtype = dtype;
+  a.stream = static_cast<hipStream_t>(stream);
+  const hipError_t e = fa::launch_bwd(a, causal);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int flash_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                   void* dq, void* dk, void* dv, float* delta, int B, int H, int N, int d, float scale, int dtype,
+                   void* stream) {
+  return flash_attn_bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N, d, scale, dtype, stream, false);
+}
+
+int flash_attn_bwd_causal(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                          const float* lse, void* dq, void* dk, void* dv, float* delta, int B, int H, int N, int d,
+                          float scale, int dtype, void* stream) {
+  return flash_attn_bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N, d, scale, dtype, stream, true);
+}
+
 size_t attn_naive_workspace_bytes(int B, int H, int N, int dtype) {
   if (B < 0 || H < 0 || N < 0) return 0;
   if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16) return 0;

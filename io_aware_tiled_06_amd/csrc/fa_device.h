@@ -42,11 +42,9 @@ template <> struct Mfma<BF16> {
     bf16x2 v = {(__bf16)x, (__bf16)y};
     return __builtin_bit_cast(uint32_t, v);
   }
-  // acc + lo + hi of a packed pair (v_dot2 against (1, 1); exact products)
-  static __device__ __forceinline__ float sum2(uint32_t pair, float acc) {
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair), __builtin_bit_cast(bf16x2, 0x3f803f80u),
-                                           acc, false);
-  }
+  // the two bf16 of a packed pair as floats (exact)
+  static __device__ __forceinline__ float lo(uint32_t pair) { return __uint_as_float(pair << 16); }
+  static __device__ __forceinline__ float hi(uint32_t pair) { return __uint_as_float(pair & 0xffff0000u); }
 };
 template <> struct Mfma<F16> {
   static __device__ __forceinline__ f32x16 run(u32x4 a, u32x4 b, f32x16 c) {
@@ -57,10 +55,16 @@ template <> struct Mfma<F16> {
     f16x2 v = {(_Float16)x, (_Float16)y};
     return __builtin_bit_cast(uint32_t, v);
   }
-  static __device__ __forceinline__ float sum2(uint32_t pair, float acc) {
-    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pair), __builtin_bit_cast(f16x2, 0x3c003c00u), acc, false);
-  }
+  static __device__ __forceinline__ float lo(uint32_t pair) { return (float)__builtin_bit_cast(f16x2, pair)[0]; }
+  static __device__ __forceinline__ float hi(uint32_t pair) { return (float)__builtin_bit_cast(f16x2, pair)[1]; }
 };
+
+// Register r of a 32x32 product in lane group g (= lane / 32) holds row
+// kb*32 + (r/4)*8 + g*4 + r%4 of the block kb it covers (the accumulator
+// layout above); for transposed scores S^T that row index is a key.
+__device__ __forceinline__ int score_key(int kb, int r, int g) {
+  return kb * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
+}
 
 // 2^x on the transcendental unit (v_exp_f32).
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -149,6 +153,20 @@ __device__ __forceinline__ void load_lds16(i32x4 rsrc, uint32_t lds, uint32_t vo
       : "memory");
 }
 
+// The same with 4 bytes per lane (buffer_load_dword ... lds): lane i fills
+// LDS bytes [lds + 4 i, lds + 4 i + 4).
+__device__ __forceinline__ void load_lds4(i32x4 rsrc, uint32_t lds, uint32_t voff) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "buffer_load_dword %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(voff), "s"(rsrc)
+      : "memory");
+}
+
 // Wait until at most N vector-memory operations of this wave are outstanding
 // (they complete in issue order). Inline assembly, so that it stays exactly
 // where it is written; the "memory" clobber keeps memory accesses on their side.
@@ -179,6 +197,10 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const char* lds) {
 //  * V (transposing 8-byte reads): 4 consecutive rows x 4 consecutive chunks
 //    -> 16 distinct slots (d = 128) / (row parity, slot) pairs (d = 64), and
 //    any 16 lanes of it -> 8 distinct slots modulo 8.
+//  * dual: a tile read both ways (the backward pass reads Q, dO and K both
+//    as 16-byte rows and transposed): an XOR-linear map of the row's low four
+//    bits, found by exhaustive search over such maps on a CPU model of both
+//    access patterns; conflict free for both, on 32 or 64 banks.
 template <int D> struct TileSwizzle;
 template <> struct TileSwizzle<128> {
   static __device__ __forceinline__ int k(int r) { return r & 15; }
@@ -186,10 +208,17 @@ template <> struct TileSwizzle<128> {
     const int t = r & 3;
     return 4 * t + 2 * (t >> 1);
   }
+  // bits (r0, r1, r0^r2, r1^r3)
+  static __device__ __forceinline__ int dual(int r) { return (r & 3) | (((r ^ (r >> 2)) & 3) << 2); }
 };
 template <> struct TileSwizzle<64> {
   static __device__ __forceinline__ int k(int r) { return (r & 7) ^ ((r >> 3) & 1); }
   static __device__ __forceinline__ int v(int r) { return 2 * (r & 3); }
+  // bits (r1, r0^r2, r0^r1^r3)
+  static __device__ __forceinline__ int dual(int r) {
+    const int b0 = (r >> 1) & 1, b1 = (r ^ (r >> 2)) & 1, b2 = (r ^ (r >> 1) ^ (r >> 3)) & 1;
+    return b0 | (b1 << 1) | (b2 << 2);
+  }
 };
 
 // Row staging: ROWS rows of ROW_BYTES bytes copied from global memory into

@@ -33,6 +33,29 @@ hipError_t launch_flash(const AttnArgs& a);
 // The same with causal masking: query i sees keys j <= i.
 hipError_t launch_flash_causal(const AttnArgs& a);
 
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  float* delta;  // caller's [B,H,N] float32 scratch
+  void* dq;
+  void* dk;
+  void* dv;
+  int B, H, N, d;
+  float scale;
+  int dtype;
+  hipStream_t stream;
+};
+
+// Rows (queries or keys) per workgroup of the backward kernels.
+int bwd_rows_per_block();
+
+// Backward pass: D = rowsum(dO * O), then dQ, then dK and dV (three launches).
+hipError_t launch_bwd(const BwdArgs& a, bool causal);
+
 // Largest number of heads one launch of the three-pass path may cover
 // (grid-size limit); 0 means N is too large for that path.
 int64_t naive_max_heads_per_launch(int N, int d, int dtype);

@@ -51,11 +51,6 @@ struct FwdParams {
   float c;       // scale * log2(e)
 };
 
-// Score of register r of 32-key block kb in lane group g is key
-// kb*32 + (r/4)*8 + g*4 + r%4 of the tile.
-__device__ __forceinline__ int score_key(int kb, int r, int g) {
-  return kb * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
-}
 
 // Hide keys at or past n (only in the last, ragged tile): they must lose the
 // row extremum. `hide` is -inf when c >= 0 (maximum) and +inf otherwise.

@@ -124,3 +124,26 @@ def test_binding_refuses_cpu_tensors():
         fa.flash_attn_fwd(x, x, x)
     with pytest.raises(ValueError, match="GPU"):
         fa.attn_naive_fwd(x, x, x)
+
+
+def bwd(L, ptrs=None, B=1, H=1, N=16, d=64, scale=0.125, dtype=2, causal=False):
+    base = [P, P2, P3, 0x70000, 0x80000, PL, 0x90000, 0xA0000, 0xB0000, 0xC0000]
+    if ptrs:
+        for i, val in ptrs.items():
+            base[i] = val
+    fn = L.flash_attn_bwd_causal if causal else L.flash_attn_bwd
+    return fn(*base, B, H, N, d, scale, dtype, None)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_validation(L, causal):
+    assert bwd(L, B=-1, causal=causal) == fa.FA_ERR_SHAPE
+    assert bwd(L, d=96, causal=causal) == fa.FA_ERR_UNSUPPORTED
+    assert bwd(L, dtype=0, causal=causal) == fa.FA_ERR_UNSUPPORTED  # float32 backward is not provided
+    assert bwd(L, scale=math.nan, causal=causal) == fa.FA_ERR_SCALE
+    for i in range(10):  # every pointer is required
+        assert bwd(L, {i: None}, causal=causal) == fa.FA_ERR_NULL, i
+    for i in (0, 3, 4, 6, 7, 8, 9):
+        assert bwd(L, {i: [P, P2, P3, 0x70000, 0x80000, PL, 0x90000, 0xA0000, 0xB0000, 0xC0000][i] + 2},
+                   causal=causal) == fa.FA_ERR_ALIGN, i
+    assert bwd(L, N=0, causal=causal) == fa.FA_OK

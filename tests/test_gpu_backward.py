@@ -1,0 +1,126 @@
+"""Backward pass on the GPU against the float64 gradient oracle.
+
+The GPU forward pass supplies O and LSE (as a caller would); the oracle
+differentiates exact attention at the same (rounded) inputs. The pages fix no
+tolerance for gradients; the bound follows the arithmetic. With u the unit
+roundoff of the element type (2^-9 for bf16, 2^-12 for fp16), per gradient
+tensor G with reference R:
+  relative RMS  ||G - R|| / ||R||            <= 5 u
+  max abs       max|G - R| / max|R|          <= 10 u
+Sources of error: P and dS are rounded to the input type before their
+products (relative u each), D = dO . O uses the forward's rounded O, and the
+gradients themselves are rounded to the input type. dV sees about one such
+rounding (measured ~1.2 u RMS), dQ and dK about two (measured ~2 u RMS, up
+to 3.8 u max for bf16, 4 u for fp16), since dS = P (dP - D) has vanishing
+row sums and amplifies the error of D.
+"""
+import math
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import io_aware_tiled_06_amd as fa  # noqa: E402
+from io_aware_tiled_06_amd.workloads import WORKLOADS, Workload, make_inputs  # noqa: E402
+from oracle import attention_backward_reference  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+TORCH_DT = {"fp16": torch.float16, "bf16": torch.bfloat16}
+UNIT = {"bf16": 2.0 ** -9, "fp16": 2.0 ** -12}
+
+
+def upstream(w, seed):
+    """dL/dO: i.i.d. N(0,1), rounded to the element type (the same values feed
+    GPU and oracle)."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((w.B, w.H, w.N, w.d), dtype=np.float32)
+    return torch.from_numpy(x).to(TORCH_DT[w.dtype]).float().numpy()
+
+
+def run_backward(w, q, k, v, do, scale, causal):
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(TORCH_DT[w.dtype]).cuda()  # noqa: E731
+    tq, tk, tv, tdo = dev(q), dev(k), dev(v), dev(do)
+    o, lse = fa.flash_attn_fwd(tq, tk, tv, scale, causal=causal)
+    dq, dk, dv = fa.flash_attn_bwd(tq, tk, tv, o, lse, tdo, scale, causal=causal)
+    torch.cuda.synchronize()
+    return tuple(t.float().cpu().numpy().astype(np.float64) for t in (dq, dk, dv))
+
+
+def check(got, ref, what, dtype):
+    rel_rms_tol, rel_max_tol = 5 * UNIT[dtype], 10 * UNIT[dtype]
+    for name, g, r in zip(("dQ", "dK", "dV"), got, ref):
+        assert np.all(np.isfinite(g)), f"{what} {name}: non-finite"
+        err = g - r
+        rel = float(np.linalg.norm(err) / max(np.linalg.norm(r), 1e-300))
+        mx = float(np.max(np.abs(err)) / max(np.max(np.abs(r)), 1e-300))
+        print(f"[bwd] {what} {name}: rel_rms={rel:.2e} rel_max={mx:.2e}", flush=True)
+        assert rel <= rel_rms_tol, f"{what} {name}: relative RMS {rel:.3e} > {rel_rms_tol:.2e}"
+        assert mx <= rel_max_tol, f"{what} {name}: max error {mx:.3e} of max |ref| > {rel_max_tol:.2e}"
+
+
+CASES = [
+    (1, 2, 256, 64, "bf16"),
+    (1, 2, 300, 128, "bf16"),
+    (2, 3, 129, 128, "fp16"),
+    (1, 4, 1000, 64, "fp16"),
+    (1, 2, 2048, 128, "bf16"),
+    (1, 1, 1, 128, "bf16"),
+    (1, 2, 33, 64, "bf16"),
+]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("B,H,N,d,dtype", CASES)
+def test_backward_matches_oracle(B, H, N, d, dtype, causal):
+    w = Workload("bwd", B, H, N, d, dtype, 3000 + N + d, 2.0)
+    q, k, v = make_inputs(w)
+    do = upstream(w, 4000 + N)
+    got = run_backward(w, q, k, v, do, w.scale, causal)
+    ref = attention_backward_reference(q, k, v, do, w.scale, causal=causal)
+    check(got, ref, f"B{B} H{H} N{N} d{d} {dtype} causal={causal}", dtype)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_named_workload_4096(causal):
+    """The 4096-token bf16 workload (B=1, H=8, d=128)."""
+    w = WORKLOADS["n4096_d128_bf16"]
+    q, k, v = make_inputs(w)
+    do = upstream(w, 41)
+    got = run_backward(w, q, k, v, do, w.scale, causal)
+    ref = attention_backward_reference(q, k, v, do, w.scale, causal=causal)
+    check(got, ref, f"n4096 causal={causal}", w.dtype)
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.2])
+def test_backward_scales(scale):
+    w = Workload("bwds", 1, 2, 200, 64, "bf16", 51, 1.5)
+    q, k, v = make_inputs(w)
+    do = upstream(w, 52)
+    got = run_backward(w, q, k, v, do, scale, False)
+    ref = attention_backward_reference(q, k, v, do, scale)
+    if scale == 0.0:  # dQ = dK = 0 exactly
+        assert np.all(got[0] == 0.0) and np.all(got[1] == 0.0)
+        err = float(np.linalg.norm(got[2] - ref[2]) / np.linalg.norm(ref[2]))
+        assert err <= 5 * UNIT["bf16"]
+    else:
+        check(got, ref, f"scale={scale}", "bf16")
+
+
+def test_backward_deterministic():
+    w = Workload("bwdd", 1, 2, 700, 128, "bf16", 61)
+    q, k, v = make_inputs(w)
+    do = upstream(w, 62)
+    a = run_backward(w, q, k, v, do, w.scale, False)
+    b = run_backward(w, q, k, v, do, w.scale, False)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+def test_backward_fp32_unsupported():
+    x = torch.zeros((1, 1, 16, 64), dtype=torch.float32, device="cuda")
+    lse = torch.zeros((1, 1, 16), dtype=torch.float32, device="cuda")
+    with pytest.raises(fa.FlashAttnError) as e:
+        fa.flash_attn_bwd(x, x, x, x, lse, x)
+    assert e.value.status == fa.FA_ERR_UNSUPPORTED
