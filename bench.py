@@ -36,12 +36,16 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 CSRC = os.path.join(ROOT, "io_aware_tiled_06_amd", "csrc")
 
 
-def kernel_source_hash() -> str:
+# The sources each timed kernel is compiled from (its own file plus the shared
+# device helpers): a counter record is only valid for the source it was taken on.
+KERNEL_SOURCES = {"flash": ("flash_fwd.hip", "fa_device.h"), "naive": ("naive.hip", "fa_device.h")}
+
+
+def kernel_source_hash(entry: str = "flash") -> str:
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
-        if name.endswith((".hip", ".h")):
-            with open(os.path.join(CSRC, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+    for name in sorted(KERNEL_SOURCES[entry]):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
 
 
@@ -54,7 +58,7 @@ def measured_traffic(workload: str, entry: str):
     except (OSError, ValueError):
         return None
     rec = data.get(f"{entry}:{workload}")
-    if not rec or rec.get("source_hash") != kernel_source_hash():
+    if not rec or rec.get("source_hash") != kernel_source_hash(entry):
         return None
     return rec.get("hbm_bytes_per_launch")
 
