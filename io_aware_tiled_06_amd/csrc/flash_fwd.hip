@@ -13,20 +13,17 @@
 // MI355X mapping:
 //  * One wave = 32 query rows. Scores are formed transposed, S^T = K Q^T, so
 //    that each lane holds one query row (lane % 32) and 16 keys per 32-key
-//    block: row statistics are in-lane, plus one exchange with the lane 32
+//    tile: row statistics are in-lane, plus one exchange with the lane 32
 //    away (permlane32 swap). The same register layout is the B operand of
 //    O^T = V^T P^T, so probabilities never leave registers.
-//  * K tiles are copied to LDS row major; V tiles are transposed on the way
-//    into LDS so the P V product reads 16-byte operands.
-//  * K/V tiles are double buffered: the next tile is fetched into registers
-//    while the current one is consumed, and written to the other LDS buffer
-//    before the one barrier per tile.
+//  * K and V tiles are copied from global memory straight into LDS (16 bytes
+//    per lane, XOR-swizzled chunks) through rings of four slots; V^T operands
+//    come from transposing LDS reads. One barrier per tile.
 //  * Softmax runs in base 2: p = 2^(c*s - m) with c = scale*log2(e), one FMA and
-//    one v_exp_f32 per score. The accumulator is rescaled only when some row's
-//    maximum grows by more than 2^8 (the running maximum may lag the true one
-//    by less than that; probabilities then stay below 2^8, well inside the
-//    range of every element type). The result is the same in exact
-//    arithmetic because numerator and denominator share the same m.
+//    one v_exp_f32 per score. The running maximum m is moved only when a
+//    tile's probabilities would grow too large (see flash_fwd_half); the
+//    result is the same in exact arithmetic because numerator and denominator
+//    share the same m.
 //  * Workgroup ids are remapped so that each XCD works on contiguous heads.
 #include <type_traits>
 
@@ -51,17 +48,6 @@ struct FwdParams {
   float c;       // scale * log2(e)
 };
 
-
-// Hide keys at or past n (only in the last, ragged tile): they must lose the
-// row extremum. `hide` is -inf when c >= 0 (maximum) and +inf otherwise.
-template <int NS>
-__device__ __forceinline__ void hide_tail(f32x16 (&s)[NS], int key0, int n, int g, float hide) {
-#pragma unroll
-  for (int kb = 0; kb < NS; ++kb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r)
-      if (key0 + score_key(kb, r, g) >= n) s[kb][r] = hide;
-}
 
 // Hide keys past `lim` (this lane's last visible key) in a tile starting at
 // key0: they must lose the row extremum.
@@ -123,25 +109,34 @@ __device__ __forceinline__ bool update_max(float m_tile, float& m_run, float& l_
 // ---------------------------------------------------------------------------
 // Half-precision inputs (bf16 / fp16): matrix cores, float32 accumulation.
 //
-// A wave owns QB blocks of 32 query rows. QB = 1 is used: two waves share
-// each SIMD and cover each other's LDS and barrier waits. (QB = 2 halves the
-// LDS reads per flop, since every K or V operand then feeds two products, but
-// needs 448 registers per lane, hence one wave per SIMD; measured slower on
-// MI355X.) Key tiles of BC = 32. K and
-// V tiles are copied from global memory straight into LDS (16 bytes per lane,
-// no register staging) with the chunk placement of TileSwizzle<D>, into a
-// ring of NBUF = 4 buffers each, three tiles ahead of use. The loop is
-// software pipelined: while the matrix cores form the scores of tile j+1, the
-// vector ALUs turn the scores of tile j into probabilities; while the cores
-// add P_j V_j into the accumulator, the vector ALUs find the row maxima of
-// tile j+1. One barrier per tile publishes the tiles two steps ahead and
-// frees the buffers the next copies overwrite.
+// A workgroup of NW waves owns NW * 32 query rows; key tiles of BC = 32. Two
+// workgroups share a CU, so every SIMD runs two waves of independent
+// workgroups. (Two 32-row blocks per wave would halve the LDS reads per
+// product but needs about 460 registers per lane, hence one wave per SIMD;
+// measured slower on MI355X, as was an 8-wave workgroup.)
+//
+// Software pipeline, step t: the matrix cores form the scores of tile t+1 and
+// add P_{t-1} V_{t-1} into the accumulator; the vector ALUs turn tile t's
+// scores into probabilities. No work of a step waits on a product issued in
+// the same step, so each wave's matrix and vector work can overlap freely and
+// the two waves of a SIMD fill each other's gaps. K tiles are copied three
+// tiles ahead and V tiles two (rings of four slots each; a slot is rewritten
+// only after the barrier that follows its last read).
+//
+// Running maximum: tile t's probabilities are first computed with m as it
+// stands. If every lane's sum of its 16 probabilities is at most 2^8, every
+// probability is at most 2^8 (they are non-negative) and the tile is done:
+// no row maximum is taken. Otherwise (in practice the tiles where a row's
+// scores jump by several units) the tile's exact maximum is found, m, the
+// running sum and the accumulator are rescaled by 2^(m_old - m_new), and the
+// tile's probabilities are recomputed, now at most 1. m therefore never
+// exceeds the running maximum and trails it by a bounded amount; P stays
+// inside the range of fp16 and bf16.
 // ---------------------------------------------------------------------------
-template <class E, int D, int NW, int QB, bool NEG, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(QB == 1 ? 2 : 1)))
+template <class E, int D, int NW, bool NEG, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void flash_fwd_half(FwdParams p) {
-  static_assert(!CAUSAL || QB == 1, "causal masking assumes one 32-row block per wave");
-  constexpr int BR = NW * 32 * QB;
+  constexpr int BR = NW * 32;
   constexpr int BC = 32;
   constexpr int NBUF = 4;
   constexpr int RB = D * 2;   // bytes per K / V row
@@ -149,6 +144,7 @@ void flash_fwd_half(FwdParams p) {
   constexpr int DB = D / 32;  // 32-feature blocks of the output
   constexpr int kTile = BC * RB;
   constexpr int kPer = kTile / 1024 / NW;  // 1 KB direct copies per wave per tile
+  constexpr float kSumLimit = 256.f;       // per lane and tile, see above
   static_assert(kTile % (1024 * NW) == 0, "a tile must split into 1 KB copies evenly over the waves");
   using Swz = TileSwizzle<D>;
   __shared__ __attribute__((aligned(1024))) char smem[2 * NBUF * kTile];  // K ring, V ring
@@ -183,13 +179,14 @@ void flash_fwd_half(FwdParams p) {
     cp_v[t] = (slot ^ Swz::v(r)) * 16;
   }
   // Copy tile `tile` of a head's K or V into `dst`. Rows at or past N (the
-  // ragged last tile only) re-read row N-1: in bounds, never used.
-  auto copy_tile = [&](const char* src, int tile, char* dst, const uint32_t(&col)[kPer]) {
+  // ragged last tile only) re-read row N-1: in bounds, never used. FULL (a
+  // compile-time tag): the caller knows the tile is whole.
+  auto copy_tile = [&](const char* src, int tile, char* dst, const uint32_t(&col)[kPer], auto full_tag) {
     const int row0 = tile * BC;
     const i32x4 rs = buffer_rsrc(src + (int64_t)row0 * RB, kTile);
     const uint32_t l0 = lds_addr(dst) + wave * kPer * 1024;
     const int last = N - 1 - row0;
-    if (last >= BC - 1) {
+    if (decltype(full_tag)::value || last >= BC - 1) {
 #pragma unroll
       for (int t = 0; t < kPer; ++t) load_lds16(rs, l0 + t * 1024, cp_row[t] * RB + col[t]);
     } else {
@@ -215,18 +212,16 @@ void flash_fwd_half(FwdParams p) {
     }
   }
 
-  // This lane's query rows (one per block); rows past the end load row N-1
-  // and are not stored. The query loads are issued before any copy (the
-  // scheduling barrier keeps them there), so the copy counts below are the
-  // last operations in the vector-memory queue.
-  int q_row[QB];
-  u32x4 qf[QB][KK];
+  // This lane's query row; rows past the end load row N-1 and are not stored.
+  // The query loads are issued before any copy (the scheduling barrier keeps
+  // them there), so the copy counts below are the last operations in the
+  // vector-memory queue.
+  const int q_row = qt * BR + wave * 32 + l32;
+  u32x4 qf[KK];
+  {
+    const int q_ld = q_row < N ? q_row : N - 1;
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    q_row[qb] = qt * BR + (wave * QB + qb) * 32 + l32;
-    const int q_ld = q_row[qb] < N ? q_row[qb] : N - 1;
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) qf[qb][kk] = ld_global16(Q + ((int64_t)q_ld * D + kk * 16 + g * 8) * 2);
+    for (int kk = 0; kk < KK; ++kk) qf[kk] = ld_global16(Q + ((int64_t)q_ld * D + kk * 16 + g * 8) * 2);
   }
   __builtin_amdgcn_sched_barrier(0);
 
@@ -240,65 +235,57 @@ void flash_fwd_half(FwdParams p) {
   const int kt_end = CAUSAL ? min(n_tiles, (qt + 1) * (BR / BC)) : n_tiles;
   const int diag = CAUSAL ? (qt * BR + wave * 32) / BC : n_tiles;
   const int my_last = min(diag, n_tiles - 1);
-  const int key_lim = CAUSAL ? min(q_row[0], N - 1) : N - 1;
-  // Ring start: tiles 0..2 of K and V.
-  for (int t = 0; t < 3; ++t)
-    if (t < kt_end) {
-      copy_tile(K, t, kbuf(t), cp_k);
-      copy_tile(V, t, vbuf(t), cp_v);
-    }
-
-  f32x16 acc[QB][DB];
-  float l_run[QB], m_run[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-#pragma unroll
-    for (int db = 0; db < DB; ++db) acc[qb][db] = f32x16{};
-    l_run[qb] = 0.f;
+  const int key_lim = CAUSAL ? min(q_row, N - 1) : N - 1;
+  using F = std::false_type;
+  // Ring start: the copies of virtual steps -3..-1 (step t copies K_{t+3} and
+  // V_{t+2}, in that order): K0; K1, V0; K2, V1.
+  for (int t = -3; t < 0; ++t) {
+    if (t + 3 < kt_end) copy_tile(K, t + 3, kbuf(t + 3), cp_k, F{});
+    if (t + 2 >= 0 && t + 2 < kt_end) copy_tile(V, t + 2, vbuf(t + 2), cp_v, F{});
   }
-  // keys past N must lose the row extremum: -inf for c >= 0, +inf for c < 0
-  constexpr float hide = NEG ? INFINITY : -INFINITY;
-  typedef f32x16 Scores[QB];
 
-  // S^T = K Q^T for one tile (32 keys x 32 queries per block).
-  auto scores = [&](const char* kb_lds, Scores& s) {
+  f32x16 acc[DB];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) s[qb] = f32x16{};
+  for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
+  float l_run = 0.f, m_run;
+  // hidden keys must lose the row extremum: -inf for c >= 0, +inf for c < 0
+  constexpr float hide = NEG ? INFINITY : -INFINITY;
+
+  // S^T = K Q^T for one tile (32 keys x 32 queries).
+  auto scores = [&](const char* kb_lds, f32x16& s) {
+    s = f32x16{};
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       const u32x4 a = *reinterpret_cast<const u32x4*>(kb_lds + k_off[kk]);
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) s[qb] = Mfma<E>::run(a, qf[qb][kk], s[qb]);
+      s = Mfma<E>::run(a, qf[kk], s);
     }
   };
-  // Probabilities of one tile, rounded to the element type: the B operand of
-  // O^T += V^T P^T (register r is key slot r % 8 of half r / 8). Their float32
-  // sum (before rounding: the row normaliser and LSE are float32) goes to l.
-  auto probs = [&](const Scores& s, u32x4(&pf)[QB][2], int key0, bool mask) {
+  // Probabilities of one tile with the current m, rounded to the element type:
+  // the B operand of O^T += V^T P^T (register r is key slot r % 8 of half
+  // r / 8). Returns their float32 sum (before rounding: the row normaliser and
+  // LSE are float32). Hidden keys get an explicit zero (with c == 0 a hidden
+  // score would give 0 * inf).
+  auto probs = [&](const f32x16& s, u32x4(&pf)[2], int key0, bool mask) {
+    float ls[2];
+    const float neg_m = -m_run;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      float ls[2];
-      const float neg_m = -m_run[qb];
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const int r = h * 8 + 2 * w;
-          float p0 = exp2_fast(fmaf(s[qb][r], c, neg_m));
-          float p1 = exp2_fast(fmaf(s[qb][r + 1], c, neg_m));
-          if (mask) {
-            // explicit zero: with c == 0 a hidden score would give 0 * inf
-            if (key0 + score_key(0, r, g) > key_lim) p0 = 0.f;
-            if (key0 + score_key(0, r + 1, g) > key_lim) p1 = 0.f;
-          }
-          pf[qb][h][w] = Mfma<E>::pack2(p0, p1);
-          ls[h] = w == 0 ? p0 + p1 : ls[h] + (p0 + p1);
+      for (int w = 0; w < 4; ++w) {
+        const int r = h * 8 + 2 * w;
+        float p0 = exp2_fast(fmaf(s[r], c, neg_m));
+        float p1 = exp2_fast(fmaf(s[r + 1], c, neg_m));
+        if (mask) {
+          if (key0 + score_key(0, r, g) > key_lim) p0 = 0.f;
+          if (key0 + score_key(0, r + 1, g) > key_lim) p1 = 0.f;
         }
-      l_run[qb] += ls[0] + ls[1];
-    }
+        pf[h][w] = Mfma<E>::pack2(p0, p1);
+        ls[h] = w == 0 ? p0 + p1 : ls[h] + (p0 + p1);
+      }
+    return ls[0] + ls[1];
   };
   // O^T += V^T P^T for one tile.
-  auto accumulate = [&](const char* vb_lds, const u32x4(&pf)[QB][2]) {
+  auto accumulate = [&](const char* vb_lds, const u32x4(&pf)[2]) {
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -306,127 +293,123 @@ void flash_fwd_half(FwdParams p) {
         const char* a = vb_lds + v_off[db] + h * 16 * RB;
         const u32x2 lo = lds_read_tr16(a), hi = lds_read_tr16(a + 8 * RB);
         const u32x4 vt = {lo[0], lo[1], hi[0], hi[1]};
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) acc[qb][db] = Mfma<E>::run(vt, pf[qb][h], acc[qb][db]);
+        acc[db] = Mfma<E>::run(vt, pf[h], acc[db]);
       }
   };
-  // Running maxima with the scores s of the next tile: moved lazily; the
-  // accumulator and the sum follow them.
-  auto advance_max = [&](const Scores& s) {
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const f32x16 one[1] = {s[qb]};
-      float alpha;
-      if (update_max(row_max_scaled_fixed<NEG>(one, c), m_run[qb], l_run[qb], alpha)) {
-#pragma unroll
-        for (int db = 0; db < DB; ++db) acc[qb][db] *= alpha;
-      }
-    }
-  };
-  auto mask_tail = [&](Scores& s, int key0) {
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      f32x16 one[1] = {s[qb]};
+  // Exact maximum of c*s over a tile for this lane's row (both lanes of the
+  // pair get the same value); hidden keys are set to `hide` first.
+  auto tile_max = [&](f32x16& s, int key0, bool mask) {
+    f32x16 one[1] = {s};
+    if (mask) {
       hide_after(one, key0, key_lim, g, hide);
-      s[qb] = one[0];
+      s = one[0];
     }
+    return row_max_scaled_fixed<NEG>(one, c);
+  };
+  // Tile t's probabilities into pf and its share of the running sum.
+  auto softmax_tile = [&](f32x16& s, u32x4(&pf)[2], int key0, bool mask) {
+    float lt = probs(s, pf, key0, mask);
+    if (__any(!(lt <= kSumLimit))) {
+      const float m_new = fmaxf(m_run, tile_max(s, key0, mask));
+      if (m_new != m_run) {
+        const float alpha = exp2_fast(m_run - m_new);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+        l_run *= alpha;
+        m_run = m_new;
+      }
+      lt = probs(s, pf, key0, mask);
+    }
+    l_run += lt;
   };
   // Tiles that need masking: the ragged last one, and (causal) the diagonal.
   auto needs_mask = [&](int t) { return t == n_full || (CAUSAL && t == diag); };
 
-  // Step 0 reads K_1 and V_0; tiles 0 and 1 have landed once at most the
-  // copies of tile 2 are in flight (vector-memory operations complete in
-  // issue order).
+  // Tiles 0 and 1 of K have landed once at most the copies V0, K2, V1 are in
+  // flight (vector-memory operations complete in issue order); with fewer
+  // than three tiles, wait for everything.
   if (kt_end > 2)
-    vm_wait<2 * kPer>();
+    vm_wait<3 * kPer>();
   else
     vm_wait<0>();
   __syncthreads();
-  Scores sa, sb;
-  scores(kbuf(0), sa);
-  if (needs_mask(0)) mask_tail(sa, 0);
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const f32x16 one[1] = {sa[qb]};
-    m_run[qb] = row_max_scaled_fixed<NEG>(one, c);
-  }
+  f32x16 sb[2];
+  u32x4 pb[2][2];
+  scores(kbuf(0), sb[0]);
+  m_run = tile_max(sb[0], 0, needs_mask(0));  // the first tile sets m exactly
 
-  // One step: tile j's probabilities and P V, tile j+1's scores and maximum.
-  // Copies of K_{j+3} and V_{j+3} go out first, into the buffers of tile
-  // j-1, which the previous barrier freed; at the end the copies of tiles
-  // j+2, issued one step earlier, must have landed before the barrier.
-  // STEADY: buffers known at compile time (B = j % NBUF), tile j+1 needs no
-  // mask for any wave, copies of this step exist. Otherwise everything is
-  // decided at run time; the workgroup-wide decisions (copies, barrier) and
-  // this wave's own (does it still work on tile j, j+1) are kept apart, so
-  // every wave passes the same barriers.
-  auto step = [&](int j, Scores& s_cur, Scores& s_nxt, auto b_tag, auto steady_tag) {
+  // One step. Copies of K_{t+3} and V_{t+2} go out first, into the slots of
+  // K_{t-1} (last read in step t-2) and V_{t-2} (last read in step t-1). At the
+  // end K_{t+2} and V_t (used by step t+1) must have landed: at most the later
+  // copies V_{t+1}, K_{t+3}, V_{t+2} may be in flight.
+  // STEADY: slots known at compile time (b = t % NBUF), every copy is of a
+  // whole tile, no tile of the step needs a mask and every wave works on all
+  // of them. Otherwise everything is decided at run time; the workgroup-wide
+  // decisions (copies, barrier) and this wave's own (does it still work on
+  // tile t, t+1) are kept apart, so every wave passes the same barriers.
+  auto step = [&](int t, f32x16& s_cur, f32x16& s_nxt, const u32x4(&p_prev)[2], u32x4(&p_cur)[2], auto slot_tag,
+                  auto steady_tag) {
     constexpr bool STEADY = decltype(steady_tag)::value;
-    const int b = STEADY ? decltype(b_tag)::value : j % NBUF;
-    const bool copies = STEADY || j + 3 < kt_end;
-    if (copies) {
-      copy_tile(K, j + 3, kbuf((b + 3) % NBUF), cp_k);
-      copy_tile(V, j + 3, vbuf((b + 3) % NBUF), cp_v);
-    }
-    const bool wg_next = STEADY || j + 1 < kt_end;
-    const bool next = STEADY || j + 1 <= my_last;
-    const bool cur = STEADY || j <= my_last;
-    if (next) scores(kbuf((b + 1) % NBUF), s_nxt);
-    if (cur) {
-      u32x4 pf[QB][2];
-      probs(s_cur, pf, j * BC, !STEADY && needs_mask(j));
-      accumulate(vbuf(b), pf);
-    }
-    if (next) {
-      if (!STEADY && needs_mask(j + 1)) mask_tail(s_nxt, (j + 1) * BC);
-      advance_max(s_nxt);
-    }
-    if (wg_next) {
-      if (copies)
-        vm_wait<2 * kPer>();
-      else
-        vm_wait<0>();
-      __syncthreads();
-    }
+    const int b = STEADY ? decltype(slot_tag)::value : t % NBUF;
+    using Full = std::integral_constant<bool, STEADY>;
+    if (STEADY || t + 3 < kt_end) copy_tile(K, t + 3, kbuf((b + 3) % NBUF), cp_k, Full{});
+    if (STEADY || t + 2 < kt_end) copy_tile(V, t + 2, vbuf((b + 2) % NBUF), cp_v, Full{});
+    if (STEADY || t + 1 <= my_last) scores(kbuf((b + 1) % NBUF), s_nxt);
+    if (STEADY || (t >= 1 && t - 1 <= my_last)) accumulate(vbuf((b + 3) % NBUF), p_prev);
+    if (STEADY || t <= my_last) softmax_tile(s_cur, p_cur, t * BC, !STEADY && needs_mask(t));
+    if (STEADY)
+      vm_wait<3 * kPer>();
+    else
+      vm_wait<0>();
+    __syncthreads();
   };
   using T = std::true_type;
-  using F = std::false_type;
-  int j = 0;
-  // steady groups: every step's copies exist (j + 3 + 3 < kt_end), the tile
-  // after the group's last one is full (j + 4 < n_full) and (causal) lies
-  // below every wave's diagonal (j + 4 < qt * BR / BC, wave 0's diagonal)
+  // run-time steps keep tile t's scores in sb[0] and P_{t-1} in pb[1]
+  auto rotate = [&]() {
+    sb[0] = sb[1];
+    pb[1][0] = pb[0][0];
+    pb[1][1] = pb[0][1];
+  };
+  step(0, sb[0], sb[1], pb[1], pb[0], std::integral_constant<int, 0>{}, F{});
+  rotate();
+  int t = 1;
+  // Steady groups of four steps from t = 1 (mod 4): copies up to tile t + 6
+  // exist and are whole, and the tiles up to t + 4 lie below every wave's
+  // diagonal (wave 0's is qt * BR / BC).
   const int steady_end = CAUSAL ? min(n_full, qt * (BR / BC)) : n_full;
-  for (; j + 6 < kt_end && j + 4 < steady_end; j += 4) {
-    step(j, sa, sb, std::integral_constant<int, 0>{}, T{});
-    step(j + 1, sb, sa, std::integral_constant<int, 1>{}, T{});
-    step(j + 2, sa, sb, std::integral_constant<int, 2>{}, T{});
-    step(j + 3, sb, sa, std::integral_constant<int, 3>{}, T{});
+#define FA_STEADY_STEP(I)                                                                      \
+  step(t + (I), sb[(I) % 2], sb[((I) + 1) % 2], pb[((I) + 1) % 2], pb[(I) % 2],               \
+       std::integral_constant<int, ((I) + 1) % NBUF>{}, T{})
+  for (; t + 6 < kt_end && t + 6 < n_full && t + 4 < steady_end; t += 4) {
+    FA_STEADY_STEP(0);
+    FA_STEADY_STEP(1);
+    FA_STEADY_STEP(2);
+    FA_STEADY_STEP(3);
   }
-  for (; j < kt_end; ++j) {
-    step(j, sa, sb, std::integral_constant<int, 0>{}, F{});
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) sa[qb] = sb[qb];
+#undef FA_STEADY_STEP
+  for (; t < kt_end; ++t) {
+    step(t, sb[0], sb[1], pb[1], pb[0], std::integral_constant<int, 0>{}, F{});
+    rotate();
   }
+  // The workgroup's last tile: its V landed before the last barrier.
+  if (kt_end - 1 <= my_last) accumulate(vbuf((kt_end - 1) % NBUF), pb[1]);
 
   // Epilogue: one division per row ("rescale once at the end"), O rounded to
   // nearest even; LSE = ln(2^m * l) = (m + log2 l) * ln 2.
+  const float l_tot = pair_sum(l_run);
+  const float inv = 1.f / l_tot;
+  if (q_row < N) {
+    char* orow = p.o + head + (int64_t)q_row * RB;
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const float l_tot = pair_sum(l_run[qb]);
-    const float inv = 1.f / l_tot;
-    if (q_row[qb] < N) {
-      char* orow = p.o + head + (int64_t)q_row[qb] * RB;
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          u32x2 w;
-          w[0] = Mfma<E>::pack2(acc[qb][db][i * 4 + 0] * inv, acc[qb][db][i * 4 + 1] * inv);
-          w[1] = Mfma<E>::pack2(acc[qb][db][i * 4 + 2] * inv, acc[qb][db][i * 4 + 3] * inv);
-          *reinterpret_cast<u32x2*>(orow + (db * 32 + i * 8 + g * 4) * 2) = w;
-        }
-      if (g == 0 && p.lse) p.lse[(int64_t)bh * N + q_row[qb]] = (m_run[qb] + log2f(l_tot)) * kLn2;
-    }
+      for (int i = 0; i < 4; ++i) {
+        u32x2 w;
+        w[0] = Mfma<E>::pack2(acc[db][i * 4 + 0] * inv, acc[db][i * 4 + 1] * inv);
+        w[1] = Mfma<E>::pack2(acc[db][i * 4 + 2] * inv, acc[db][i * 4 + 3] * inv);
+        *reinterpret_cast<u32x2*>(orow + (db * 32 + i * 8 + g * 4) * 2) = w;
+      }
+    if (g == 0 && p.lse) p.lse[(int64_t)bh * N + q_row] = (m_run + log2f(l_tot)) * kLn2;
   }
 }
 
@@ -569,12 +552,11 @@ __global__ __launch_bounds__(NW * 64) void flash_fwd_f32(FwdParams p) {
 
 // Tile configuration per (element type, head size).
 constexpr int kWavesHalf = 4;
-constexpr int kQueryBlocksHalf = 1;
 constexpr int kWavesF32 = 4;
 
-template <class E, int D, int QB, bool CAUSAL>
+template <class E, int D, bool CAUSAL>
 hipError_t run_half(const AttnArgs& a) {
-  constexpr int BR = kWavesHalf * 32 * QB;
+  constexpr int BR = kWavesHalf * 32;
   FwdParams p;
   p.q = static_cast<const char*>(a.q);
   p.k = static_cast<const char*>(a.k);
@@ -586,10 +568,10 @@ hipError_t run_half(const AttnArgs& a) {
   p.n_blocks = a.B * a.H * p.n_qtiles;
   p.c = a.scale * kLog2e;
   if (a.scale < 0.f)
-    hipLaunchKernelGGL((flash_fwd_half<E, D, kWavesHalf, QB, true, CAUSAL>), dim3(p.n_blocks),
+    hipLaunchKernelGGL((flash_fwd_half<E, D, kWavesHalf, true, CAUSAL>), dim3(p.n_blocks),
                        dim3(kWavesHalf * 64), 0, a.stream, p);
   else
-    hipLaunchKernelGGL((flash_fwd_half<E, D, kWavesHalf, QB, false, CAUSAL>), dim3(p.n_blocks),
+    hipLaunchKernelGGL((flash_fwd_half<E, D, kWavesHalf, false, CAUSAL>), dim3(p.n_blocks),
                        dim3(kWavesHalf * 64), 0, a.stream, p);
   return hipGetLastError();
 }
@@ -613,16 +595,15 @@ hipError_t run_f32(const AttnArgs& a) {
 
 }  // namespace
 
-int flash_rows_per_block(int dtype, int /*d*/) { return dtype == kF32 ? kWavesF32 * 32 : kWavesHalf * 32 * kQueryBlocksHalf; }
+int flash_rows_per_block(int dtype, int /*d*/) { return dtype == kF32 ? kWavesF32 * 32 : kWavesHalf * 32; }
 
 template <bool CAUSAL>
 hipError_t launch(const AttnArgs& a) {
-  constexpr int QB = kQueryBlocksHalf;
   switch (a.dtype) {
     case kBF16:
-      return a.d == 128 ? run_half<BF16, 128, QB, CAUSAL>(a) : run_half<BF16, 64, QB, CAUSAL>(a);
+      return a.d == 128 ? run_half<BF16, 128, CAUSAL>(a) : run_half<BF16, 64, CAUSAL>(a);
     case kF16:
-      return a.d == 128 ? run_half<F16, 128, QB, CAUSAL>(a) : run_half<F16, 64, QB, CAUSAL>(a);
+      return a.d == 128 ? run_half<F16, 128, CAUSAL>(a) : run_half<F16, 64, CAUSAL>(a);
     default:
       return a.d == 128 ? run_f32<128, CAUSAL>(a) : run_f32<64, CAUSAL>(a);
   }
