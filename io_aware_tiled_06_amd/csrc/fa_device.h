@@ -136,6 +136,11 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // LDS (buffer_load_dwordx4 ... lds): lane i fills LDS bytes
 // [lds + 16 i, lds + 16 i + 16); `lds` is wave-uniform and goes through M0,
 // which is restored afterwards. Completion is counted by vmcnt.
+// An SALU write of M0 needs one wait state before an LDS-direct load reads
+// it (the "manually inserted wait states" rule of the gfx9 family ISA); the
+// s_nop provides it, since the compiler's hazard checks do not see inside
+// inline assembly. Without it the load may use the previous M0 and write its
+// 16 bytes to the wrong LDS slot.
 // Issued as inline assembly on purpose: the compiler then does not know that
 // this load writes LDS, and does not put a full vmcnt wait in front of every
 // later transposing LDS read (it cannot tell them apart from the copy's
@@ -146,6 +151,7 @@ __device__ __forceinline__ void load_lds16(i32x4 rsrc, uint32_t lds, uint32_t vo
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
       "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
       "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
@@ -160,6 +166,7 @@ __device__ __forceinline__ void load_lds4(i32x4 rsrc, uint32_t lds, uint32_t vof
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
       "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
       "buffer_load_dword %2, %3, 0 offen lds\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)

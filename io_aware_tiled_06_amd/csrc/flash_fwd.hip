@@ -119,9 +119,11 @@ __device__ __forceinline__ bool update_max(float m_tile, float& m_run, float& l_
 // add P_{t-1} V_{t-1} into the accumulator; the vector ALUs turn tile t's
 // scores into probabilities. No work of a step waits on a product issued in
 // the same step, so each wave's matrix and vector work can overlap freely and
-// the two waves of a SIMD fill each other's gaps. K tiles are copied three
+// the two waves of a SIMD fill each other's gaps. K tiles are copied four
 // tiles ahead and V tiles two (rings of four slots each; a slot is rewritten
-// only after the barrier that follows its last read).
+// only after the barrier that follows its last read). The first two K
+// operands of the next step's score product are read from LDS during the
+// current step, so the matrix cores start each step without waiting on LDS.
 //
 // Running maximum: tile t's probabilities are first computed with m as it
 // stands. If every lane's sum of its 16 probabilities is at most 2^8, every
@@ -237,10 +239,10 @@ void flash_fwd_half(FwdParams p) {
   const int my_last = min(diag, n_tiles - 1);
   const int key_lim = CAUSAL ? min(q_row, N - 1) : N - 1;
   using F = std::false_type;
-  // Ring start: the copies of virtual steps -3..-1 (step t copies K_{t+3} and
-  // V_{t+2}, in that order): K0; K1, V0; K2, V1.
-  for (int t = -3; t < 0; ++t) {
-    if (t + 3 < kt_end) copy_tile(K, t + 3, kbuf(t + 3), cp_k, F{});
+  // Ring start: the copies of virtual steps -4..-1 (step t copies K_{t+4} and
+  // V_{t+2}, in that order): K0; K1; K2, V0; K3, V1.
+  for (int t = -4; t < 0; ++t) {
+    if (t + 4 < kt_end) copy_tile(K, t + 4, kbuf(t + 4), cp_k, F{});
     if (t + 2 >= 0 && t + 2 < kt_end) copy_tile(V, t + 2, vbuf(t + 2), cp_v, F{});
   }
 
@@ -251,12 +253,19 @@ void flash_fwd_half(FwdParams p) {
   // hidden keys must lose the row extremum: -inf for c >= 0, +inf for c < 0
   constexpr float hide = NEG ? INFINITY : -INFINITY;
 
-  // S^T = K Q^T for one tile (32 keys x 32 queries).
+  // S^T = K Q^T for one tile (32 keys x 32 queries); its first KP operands
+  // were read one step earlier (prefetch_k).
+  constexpr int KP = 2;
+  u32x4 pre_k[KP];
+  auto prefetch_k = [&](const char* kb_lds) {
+#pragma unroll
+    for (int kk = 0; kk < KP; ++kk) pre_k[kk] = *reinterpret_cast<const u32x4*>(kb_lds + k_off[kk]);
+  };
   auto scores = [&](const char* kb_lds, f32x16& s) {
     s = f32x16{};
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
-      const u32x4 a = *reinterpret_cast<const u32x4*>(kb_lds + k_off[kk]);
+      const u32x4 a = kk < KP ? pre_k[kk < KP ? kk : 0] : *reinterpret_cast<const u32x4*>(kb_lds + k_off[kk]);
       s = Mfma<E>::run(a, qf[kk], s);
     }
   };
@@ -325,23 +334,27 @@ void flash_fwd_half(FwdParams p) {
   // Tiles that need masking: the ragged last one, and (causal) the diagonal.
   auto needs_mask = [&](int t) { return t == n_full || (CAUSAL && t == diag); };
 
-  // Tiles 0 and 1 of K have landed once at most the copies V0, K2, V1 are in
+  // K0, K1, K2 and V0 have landed once at most the copies K3, V1 are in
   // flight (vector-memory operations complete in issue order); with fewer
-  // than three tiles, wait for everything.
-  if (kt_end > 2)
-    vm_wait<3 * kPer>();
+  // than four tiles, wait for everything.
+  if (kt_end > 3)
+    vm_wait<2 * kPer>();
   else
     vm_wait<0>();
   __syncthreads();
   f32x16 sb[2];
   u32x4 pb[2][2];
+  prefetch_k(kbuf(0));
   scores(kbuf(0), sb[0]);
   m_run = tile_max(sb[0], 0, needs_mask(0));  // the first tile sets m exactly
+  prefetch_k(kbuf(1));
+  __syncthreads();  // step 0 copies K_4 into K_0's slot, which every wave has now read
 
-  // One step. Copies of K_{t+3} and V_{t+2} go out first, into the slots of
-  // K_{t-1} (last read in step t-2) and V_{t-2} (last read in step t-1). At the
-  // end K_{t+2} and V_t (used by step t+1) must have landed: at most the later
-  // copies V_{t+1}, K_{t+3}, V_{t+2} may be in flight.
+  // One step. Copies of K_{t+4} and V_{t+2} go out first, into the slots of
+  // K_t (last read in step t-1) and V_{t-2} (last read in step t-1). During the
+  // step the first operands of K_{t+2} are read ahead. At the end K_{t+3} and
+  // V_{t+1} (read by step t+1) must have landed: at most this step's copies
+  // may be in flight.
   // STEADY: slots known at compile time (b = t % NBUF), every copy is of a
   // whole tile, no tile of the step needs a mask and every wave works on all
   // of them. Otherwise everything is decided at run time; the workgroup-wide
@@ -352,13 +365,14 @@ void flash_fwd_half(FwdParams p) {
     constexpr bool STEADY = decltype(steady_tag)::value;
     const int b = STEADY ? decltype(slot_tag)::value : t % NBUF;
     using Full = std::integral_constant<bool, STEADY>;
-    if (STEADY || t + 3 < kt_end) copy_tile(K, t + 3, kbuf((b + 3) % NBUF), cp_k, Full{});
+    if (STEADY || t + 4 < kt_end) copy_tile(K, t + 4, kbuf(b), cp_k, Full{});
     if (STEADY || t + 2 < kt_end) copy_tile(V, t + 2, vbuf((b + 2) % NBUF), cp_v, Full{});
     if (STEADY || t + 1 <= my_last) scores(kbuf((b + 1) % NBUF), s_nxt);
     if (STEADY || (t >= 1 && t - 1 <= my_last)) accumulate(vbuf((b + 3) % NBUF), p_prev);
+    prefetch_k(kbuf((b + 2) % NBUF));  // stale (unused) past the last tile
     if (STEADY || t <= my_last) softmax_tile(s_cur, p_cur, t * BC, !STEADY && needs_mask(t));
     if (STEADY)
-      vm_wait<3 * kPer>();
+      vm_wait<2 * kPer>();
     else
       vm_wait<0>();
     __syncthreads();
@@ -373,14 +387,14 @@ void flash_fwd_half(FwdParams p) {
   step(0, sb[0], sb[1], pb[1], pb[0], std::integral_constant<int, 0>{}, F{});
   rotate();
   int t = 1;
-  // Steady groups of four steps from t = 1 (mod 4): copies up to tile t + 6
+  // Steady groups of four steps from t = 1 (mod 4): copies up to tile t + 7
   // exist and are whole, and the tiles up to t + 4 lie below every wave's
   // diagonal (wave 0's is qt * BR / BC).
   const int steady_end = CAUSAL ? min(n_full, qt * (BR / BC)) : n_full;
 #define FA_STEADY_STEP(I)                                                                      \
   step(t + (I), sb[(I) % 2], sb[((I) + 1) % 2], pb[((I) + 1) % 2], pb[(I) % 2],               \
        std::integral_constant<int, ((I) + 1) % NBUF>{}, T{})
-  for (; t + 6 < kt_end && t + 6 < n_full && t + 4 < steady_end; t += 4) {
+  for (; t + 7 < kt_end && t + 7 < n_full && t + 4 < steady_end; t += 4) {
     FA_STEADY_STEP(0);
     FA_STEADY_STEP(1);
     FA_STEADY_STEP(2);

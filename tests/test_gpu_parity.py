@@ -195,6 +195,24 @@ def test_deterministic():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_deterministic_full_load(causal):
+    """Bitwise-equal results over repeated launches at the long-context size
+    (B=1, H=16, N=32768, d=128: 4096 workgroups, every CU busy), where a
+    missing wait or barrier between a tile's LDS copy and its readers would
+    show as a few rows that differ from run to run."""
+    gen = torch.Generator(device="cuda").manual_seed(11)
+    shape = (1, 16, 32768, 128)
+    tq = (3.0 * torch.randn(shape, generator=gen, device="cuda")).to(torch.bfloat16)
+    tk = (3.0 * torch.randn(shape, generator=gen, device="cuda")).to(torch.bfloat16)
+    tv = torch.randn(shape, generator=gen, device="cuda").to(torch.bfloat16)
+    o0, l0 = fa.flash_attn_fwd(tq, tk, tv, causal=causal)
+    for _ in range(4):
+        o, l = fa.flash_attn_fwd(tq, tk, tv, causal=causal)
+        torch.cuda.synchronize()
+        assert torch.equal(o, o0) and torch.equal(l, l0)
+
+
 def test_without_lse_and_with_out_tensor():
     w = Workload("nolse", 2, 2, 200, 128, "bf16", 8)
     q, k, v = make_inputs(w)
