@@ -134,10 +134,19 @@ __device__ __forceinline__ bool update_max(float m_tile, float& m_run, float& l_
 // tile's probabilities are recomputed, now at most 1. m therefore never
 // exceeds the running maximum and trails it by a bounded amount; P stays
 // inside the range of fp16 and bf16.
+//
+// Small grids (SPLIT = 2): when there are fewer query tiles than two per CU,
+// one wave per SIMD would be all the chip runs. The workgroup then has two
+// groups of NW waves over the same query rows; group 0 takes the first half
+// of the key tiles and group 1 the second, each through its own pair of
+// rings. At the end group 1 hands its (m, l, accumulator) to group 0 through
+// LDS, which merges the two partial softmaxes exactly (the same rescaling
+// the running maximum uses) and writes the result.
 // ---------------------------------------------------------------------------
-template <class E, int D, int NW, bool NEG, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
+template <class E, int D, int NW, int SPLIT, bool NEG, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64 * SPLIT) __attribute__((amdgpu_waves_per_eu(2)))
 void flash_fwd_half(FwdParams p) {
+  static_assert(SPLIT == 1 || SPLIT == 2, "one or two key groups");
   constexpr int BR = NW * 32;
   constexpr int BC = 32;
   constexpr int NBUF = 4;
@@ -149,13 +158,16 @@ void flash_fwd_half(FwdParams p) {
   constexpr float kSumLimit = 256.f;       // per lane and tile, see above
   static_assert(kTile % (1024 * NW) == 0, "a tile must split into 1 KB copies evenly over the waves");
   using Swz = TileSwizzle<D>;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * NBUF * kTile];  // K ring, V ring
-  auto kbuf = [&](int b) { return smem + b * kTile; };
-  auto vbuf = [&](int b) { return smem + (NBUF + b) * kTile; };
+  __shared__ __attribute__((aligned(1024))) char smem[SPLIT * 2 * NBUF * kTile];  // per group: K ring, V ring
 
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave_id = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = SPLIT == 1 ? 0 : wave_id / NW;         // key group
+  const int wave = SPLIT == 1 ? wave_id : wave_id % NW;  // position of the wave's 32 rows
   const int l32 = lane & 31, g = lane >> 5;
+  char* const gsmem = smem + grp * 2 * NBUF * kTile;
+  auto kbuf = [&](int b) { return gsmem + b * kTile; };
+  auto vbuf = [&](int b) { return gsmem + (NBUF + b) * kTile; };
   const int blk = xcd_remap(blockIdx.x, p.n_blocks);
   const int bh = blk / p.n_qtiles;
   // causal: the last query tiles of a head have the most keys; start them first
@@ -234,16 +246,27 @@ void flash_fwd_half(FwdParams p) {
   // causal attention the diagonal tile `diag` (its 32 rows start at key
   // 32 diag), where keys after each row's own position are hidden; and
   // `key_lim` is this lane's last visible key.
+  //
+  // Below, t counts this group's key tiles: local tile t is tile kt0 + t of
+  // the head, for t < cnt. The workgroup runs `steps` steps (the larger
+  // group's count); `last` is the last local tile this wave works on (-1: none).
   const int kt_end = CAUSAL ? min(n_tiles, (qt + 1) * (BR / BC)) : n_tiles;
   const int diag = CAUSAL ? (qt * BR + wave * 32) / BC : n_tiles;
-  const int my_last = min(diag, n_tiles - 1);
   const int key_lim = CAUSAL ? min(q_row, N - 1) : N - 1;
+  const int half = (kt_end + 1) / 2;
+  const int kt0 = SPLIT == 2 && grp == 1 ? half : 0;
+  const int cnt = SPLIT == 1 ? kt_end : (grp == 1 ? kt_end - half : half);
+  const int steps = SPLIT == 1 ? kt_end : half;
+  // (causal: the wave's diagonal tile, if it falls in this group's range)
+  const int last = CAUSAL ? min(diag, kt0 + cnt - 1) - kt0 : cnt - 1;
+  // whole tiles of every group, counted from its start
+  const int full_all = SPLIT == 1 ? min(kt_end, n_full) : min(kt_end - half, n_full - half);
   using F = std::false_type;
   // Ring start: the copies of virtual steps -4..-1 (step t copies K_{t+4} and
   // V_{t+2}, in that order): K0; K1; K2, V0; K3, V1.
   for (int t = -4; t < 0; ++t) {
-    if (t + 4 < kt_end) copy_tile(K, t + 4, kbuf(t + 4), cp_k, F{});
-    if (t + 2 >= 0 && t + 2 < kt_end) copy_tile(V, t + 2, vbuf(t + 2), cp_v, F{});
+    if (t + 4 < cnt) copy_tile(K, kt0 + t + 4, kbuf(t + 4), cp_k, F{});
+    if (t + 2 >= 0 && t + 2 < cnt) copy_tile(V, kt0 + t + 2, vbuf(t + 2), cp_v, F{});
   }
 
   f32x16 acc[DB];
@@ -332,21 +355,24 @@ void flash_fwd_half(FwdParams p) {
     l_run += lt;
   };
   // Tiles that need masking: the ragged last one, and (causal) the diagonal.
-  auto needs_mask = [&](int t) { return t == n_full || (CAUSAL && t == diag); };
+  auto needs_mask = [&](int t) { return kt0 + t == n_full || (CAUSAL && kt0 + t == diag); };
 
   // K0, K1, K2 and V0 have landed once at most the copies K3, V1 are in
   // flight (vector-memory operations complete in issue order); with fewer
   // than four tiles, wait for everything.
-  if (kt_end > 3)
+  if (cnt > 3)
     vm_wait<2 * kPer>();
   else
     vm_wait<0>();
   __syncthreads();
   f32x16 sb[2];
   u32x4 pb[2][2];
-  prefetch_k(kbuf(0));
-  scores(kbuf(0), sb[0]);
-  m_run = tile_max(sb[0], 0, needs_mask(0));  // the first tile sets m exactly
+  m_run = -INFINITY;
+  if (last >= 0) {
+    prefetch_k(kbuf(0));
+    scores(kbuf(0), sb[0]);
+    m_run = tile_max(sb[0], kt0 * BC, needs_mask(0));  // the first tile sets m exactly
+  }
   prefetch_k(kbuf(1));
   __syncthreads();  // step 0 copies K_4 into K_0's slot, which every wave has now read
 
@@ -365,12 +391,12 @@ void flash_fwd_half(FwdParams p) {
     constexpr bool STEADY = decltype(steady_tag)::value;
     const int b = STEADY ? decltype(slot_tag)::value : t % NBUF;
     using Full = std::integral_constant<bool, STEADY>;
-    if (STEADY || t + 4 < kt_end) copy_tile(K, t + 4, kbuf(b), cp_k, Full{});
-    if (STEADY || t + 2 < kt_end) copy_tile(V, t + 2, vbuf((b + 2) % NBUF), cp_v, Full{});
-    if (STEADY || t + 1 <= my_last) scores(kbuf((b + 1) % NBUF), s_nxt);
-    if (STEADY || (t >= 1 && t - 1 <= my_last)) accumulate(vbuf((b + 3) % NBUF), p_prev);
+    if (STEADY || t + 4 < cnt) copy_tile(K, kt0 + t + 4, kbuf(b), cp_k, Full{});
+    if (STEADY || t + 2 < cnt) copy_tile(V, kt0 + t + 2, vbuf((b + 2) % NBUF), cp_v, Full{});
+    if (STEADY || t + 1 <= last) scores(kbuf((b + 1) % NBUF), s_nxt);
+    if (STEADY || (t >= 1 && t - 1 <= last)) accumulate(vbuf((b + 3) % NBUF), p_prev);
     prefetch_k(kbuf((b + 2) % NBUF));  // stale (unused) past the last tile
-    if (STEADY || t <= my_last) softmax_tile(s_cur, p_cur, t * BC, !STEADY && needs_mask(t));
+    if (STEADY || t <= last) softmax_tile(s_cur, p_cur, (kt0 + t) * BC, !STEADY && needs_mask(t));
     if (STEADY)
       vm_wait<2 * kPer>();
     else
@@ -387,26 +413,58 @@ void flash_fwd_half(FwdParams p) {
   step(0, sb[0], sb[1], pb[1], pb[0], std::integral_constant<int, 0>{}, F{});
   rotate();
   int t = 1;
-  // Steady groups of four steps from t = 1 (mod 4): copies up to tile t + 7
-  // exist and are whole, and the tiles up to t + 4 lie below every wave's
-  // diagonal (wave 0's is qt * BR / BC).
-  const int steady_end = CAUSAL ? min(n_full, qt * (BR / BC)) : n_full;
+  // Steady groups of four steps from t = 1 (mod 4): in every group, copies up
+  // to local tile t + 7 exist and are whole, and (causal) the tiles up to
+  // t + 4 lie below every wave's diagonal (wave 0's is qt * BR / BC; the
+  // second group's tiles start at `half`).
+  const int steady_end =
+      (CAUSAL ? min(n_full, qt * (BR / BC)) : n_full) - (SPLIT == 2 ? half : 0);
 #define FA_STEADY_STEP(I)                                                                      \
   step(t + (I), sb[(I) % 2], sb[((I) + 1) % 2], pb[((I) + 1) % 2], pb[(I) % 2],               \
        std::integral_constant<int, ((I) + 1) % NBUF>{}, T{})
-  for (; t + 7 < kt_end && t + 7 < n_full && t + 4 < steady_end; t += 4) {
+  for (; t + 7 < full_all && t + 4 < steady_end; t += 4) {
     FA_STEADY_STEP(0);
     FA_STEADY_STEP(1);
     FA_STEADY_STEP(2);
     FA_STEADY_STEP(3);
   }
 #undef FA_STEADY_STEP
-  for (; t < kt_end; ++t) {
+  for (; t < steps; ++t) {
     step(t, sb[0], sb[1], pb[1], pb[0], std::integral_constant<int, 0>{}, F{});
     rotate();
   }
-  // The workgroup's last tile: its V landed before the last barrier.
-  if (kt_end - 1 <= my_last) accumulate(vbuf((kt_end - 1) % NBUF), pb[1]);
+  // P V of this wave's last tile if no step followed it (its V landed before
+  // the last barrier).
+  if (last >= 0 && last == steps - 1) accumulate(vbuf(last % NBUF), pb[1]);
+
+  if constexpr (SPLIT == 2) {
+    // Group 1 hands (m, l, accumulator) to group 0 through LDS (the rings are
+    // free once every wave has passed the barrier); lane-major per wave.
+    constexpr int kX = 2 + 16 * DB;
+    static_assert(NW * kX * 64 * 4 <= SPLIT * 2 * NBUF * kTile, "exchange must fit in the rings");
+    float* const xch = reinterpret_cast<float*>(smem) + wave * kX * 64 + lane;
+    __syncthreads();
+    if (grp == 1) {
+      xch[0] = m_run;
+      xch[64] = l_run;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xch[(2 + db * 16 + r) * 64] = acc[db][r];
+    }
+    __syncthreads();
+    if (grp == 1) return;
+    const float m1 = xch[0], l1 = xch[64];
+    const float m_new = fmaxf(m_run, m1);
+    const float a0 = m_run == m_new ? 1.f : exp2_fast(m_run - m_new);
+    const float a1 = m1 == m_new ? 1.f : exp2_fast(m1 - m_new);
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[db][r] = a0 * acc[db][r] + a1 * xch[(2 + db * 16 + r) * 64];
+    l_run = a0 * l_run + a1 * l1;
+    m_run = m_new;
+  }
 
   // Epilogue: one division per row ("rescale once at the end"), O rounded to
   // nearest even; LSE = ln(2^m * l) = (m + log2 l) * ln 2.
@@ -568,6 +626,19 @@ __global__ __launch_bounds__(NW * 64) void flash_fwd_f32(FwdParams p) {
 constexpr int kWavesHalf = 4;
 constexpr int kWavesF32 = 4;
 
+// Compute units of the current device (cached per device).
+int device_cus() {
+  static int cus[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
 template <class E, int D, bool CAUSAL>
 hipError_t run_half(const AttnArgs& a) {
   constexpr int BR = kWavesHalf * 32;
@@ -581,11 +652,21 @@ hipError_t run_half(const AttnArgs& a) {
   p.n_qtiles = (a.N + BR - 1) / BR;
   p.n_blocks = a.B * a.H * p.n_qtiles;
   p.c = a.scale * kLog2e;
+  // fewer query tiles than two per CU: split each tile's keys over two wave groups
+  if (p.n_blocks < 2 * device_cus()) {
+    if (a.scale < 0.f)
+      hipLaunchKernelGGL((flash_fwd_half<E, D, kWavesHalf, 2, true, CAUSAL>), dim3(p.n_blocks),
+                         dim3(kWavesHalf * 64 * 2), 0, a.stream, p);
+    else
+      hipLaunchKernelGGL((flash_fwd_half<E, D, kWavesHalf, 2, false, CAUSAL>), dim3(p.n_blocks),
+                         dim3(kWavesHalf * 64 * 2), 0, a.stream, p);
+    return hipGetLastError();
+  }
   if (a.scale < 0.f)
-    hipLaunchKernelGGL((flash_fwd_half<E, D, kWavesHalf, true, CAUSAL>), dim3(p.n_blocks),
+    hipLaunchKernelGGL((flash_fwd_half<E, D, kWavesHalf, 1, true, CAUSAL>), dim3(p.n_blocks),
                        dim3(kWavesHalf * 64), 0, a.stream, p);
   else
-    hipLaunchKernelGGL((flash_fwd_half<E, D, kWavesHalf, false, CAUSAL>), dim3(p.n_blocks),
+    hipLaunchKernelGGL((flash_fwd_half<E, D, kWavesHalf, 1, false, CAUSAL>), dim3(p.n_blocks),
                        dim3(kWavesHalf * 64), 0, a.stream, p);
   return hipGetLastError();
 }
