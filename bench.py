@@ -310,7 +310,7 @@ def main() -> int:
         gen = torch.Generator(device=dev).manual_seed(w.seed + 100)
         dout = torch.randn(tq.shape, generator=gen, device=dev, dtype=torch.float32).to(tdt)
         grads = [torch.empty_like(tq) for _ in range(3)]
-        delta = torch.empty(lse.shape, dtype=torch.float32, device=dev)
+        delta = torch.empty((2,) + tuple(lse.shape), dtype=torch.float32, device=dev)
         step = lambda: fa.flash_attn_bwd(tq, tk, tv, o, lse, dout, w.scale, causal=args.causal,  # noqa: E731
                                          dq=grads[0], dk=grads[1], dv=grads[2], delta=delta)
     else:

@@ -108,8 +108,9 @@ int flash_attn_fwd_causal(const void* q, const void* k, const void* v, void* o, 
  * Arguments: q, k, v, o, dout, dq, dk, dv: [B,H,N,d] device pointers of
  * `dtype` (FA_F16 or FA_BF16; FA_F32 returns FA_ERR_UNSUPPORTED); lse: the
  * [B,H,N] float32 output of the forward pass with the same inputs and scale;
- * delta: caller-owned [B,H,N] float32 scratch, overwritten with D (the
- * library allocates nothing). All 16-byte aligned; outputs must not alias
+ * delta: caller-owned float32 scratch of 2*B*H*N elements, overwritten with
+ * D ([B,H,N], first half) and LSE*log2(e) ([B,H,N], second half); the
+ * library allocates nothing. All 16-byte aligned; outputs must not alias
  * inputs. Three kernels run in order on `stream`. Arithmetic: products on the
  * matrix cores with float32 accumulation, P and dS rounded to the input type
  * before their products, gradients rounded to nearest even. Deterministic

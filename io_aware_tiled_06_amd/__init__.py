@@ -172,7 +172,8 @@ def flash_attn_bwd(q, k, v, o, lse, dout, scale=None, *, causal=False, dq=None, 
     q, k, v, o, dout: contiguous [B, H, N, d] float16/bfloat16 tensors on one
     GPU; lse: the float32 [B, H, N] LSE that flash_attn_fwd returned for these
     inputs (and the same `causal`). dq, dk, dv default to new tensors like q;
-    delta (float32 [B, H, N] scratch) to a new tensor. Returns (dq, dk, dv).
+    delta (float32 scratch of 2 * B * H * N elements) to a new tensor. Returns
+    (dq, dk, dv).
     """
     import torch
 
@@ -191,7 +192,10 @@ def flash_attn_bwd(q, k, v, o, lse, dout, scale=None, *, causal=False, dq=None, 
         if t.shape != q.shape or t.dtype != q.dtype or t.device != q.device or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous tensor of q's shape, dtype and device")
     if delta is None:
-        delta = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+        delta = torch.empty((2, B, H, N), dtype=torch.float32, device=q.device)
+    elif (delta.dtype != torch.float32 or delta.device != q.device or not delta.is_contiguous()
+          or delta.numel() < 2 * B * H * N):
+        raise ValueError("delta must be a contiguous float32 tensor of at least 2*B*H*N elements on q's device")
     fn = lib().flash_attn_bwd_causal if causal else lib().flash_attn_bwd
     with torch.cuda.device(q.device):
         st = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),

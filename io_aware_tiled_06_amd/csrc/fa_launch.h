@@ -40,7 +40,7 @@ struct BwdArgs {
   const void* o;
   const void* dout;
   const float* lse;
-  float* delta;  // caller's [B,H,N] float32 scratch
+  float* delta;  // caller's float32 scratch: D [B,H,N], then LSE*log2(e) [B,H,N]
   void* dq;
   void* dk;
   void* dv;

@@ -21,9 +21,12 @@
 //    owns 32 keys and keeps K^T and V^T in registers; per 32-query tile it
 //    forms S = Q K^T and dP = dO V^T (lane = key, registers = queries),
 //    dV^T += dO^T P and dK^T += Q^T dS, with dO^T and Q^T read transposed.
-// Streamed tiles travel global -> LDS directly (buffer_load ... lds) through a
-// 4-slot ring, three tiles ahead; tiles read both as rows and transposed use
-// the `dual` chunk swizzle.
+// Streamed tiles travel global -> LDS directly (buffer_load ... lds) through
+// rings of LDS slots; tiles read both as rows and transposed use the `dual`
+// chunk swizzle. Both kernels are software pipelined: in step t the matrix
+// cores form S and dP of tile t+1 and add the gradient products of tile t-1,
+// while the vector ALUs turn tile t's S and dP into P and dS. No work of a
+// step waits on a product issued in the same step.
 #include "fa_device.h"
 #include "fa_launch.h"
 
@@ -39,6 +42,7 @@ struct BwdParams {
   const char* dout;
   const float* lse;  // forward's natural-log row normaliser [B,H,N]
   float* delta;      // D [B,H,N], written by bwd_delta, read by the others
+  float* lse2;       // LSE * log2(e) [B,H,N], written by bwd_delta
   char* dq;
   char* dk;
   char* dv;
@@ -54,6 +58,8 @@ constexpr int kBwdRows = kBwdWaves * 32;  // rows (queries or keys) per workgrou
 
 // ---------------------------------------------------------------------------
 // D_i = sum_d dO[i][d] * O[i][d], float32. D/8 lanes per row, 16 bytes each.
+// Also LSE_i * log2(e), the row statistic in the base-2 units of P = 2^(c s -
+// LSE log2 e), so that the other kernels read it ready to use.
 // ---------------------------------------------------------------------------
 template <class E, int D>
 __global__ __launch_bounds__(256) void bwd_delta(BwdParams p, int64_t rows) {
@@ -72,7 +78,10 @@ __global__ __launch_bounds__(256) void bwd_delta(BwdParams p, int64_t rows) {
   }
 #pragma unroll
   for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
-  if (row < rows && lane % LPR == 0) p.delta[row] = acc;
+  if (row < rows && lane % LPR == 0) {
+    p.delta[row] = acc;
+    p.lse2[row] = p.lse[row] * kLog2e;
+  }
 }
 
 // Direct-copy bookkeeping shared by both kernels: copy t of a wave fills 1 KB
@@ -177,9 +186,15 @@ __device__ __forceinline__ void store_rows_t(char* head, int row, int n, int g, 
 
 // ---------------------------------------------------------------------------
 // dQ: one workgroup per 128 query rows; K and V tiles streamed.
+//
+// K tile t is read twice: as rows for S(t) in step t-1 and transposed for
+// dQ += K^T dS(t) in step t+1; V tile t once, for dP(t) in step t-1. Step t
+// copies K_{t+2} into K_{t-2}'s slot (last read in step t-1) and V_{t+3} into
+// V_{t-1}'s (last read in step t-2); at its end K_{t+2} and V_{t+2} (read in
+// step t+1) must have landed: at most this step's V copies may be in flight.
 // ---------------------------------------------------------------------------
 template <class E, int D, bool CAUSAL>
-__global__ __launch_bounds__(kBwdWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(kBwdWaves * 64) __attribute__((amdgpu_waves_per_eu(CAUSAL && D == 128 ? 1 : 2)))
 void bwd_dq(BwdParams p) {
   constexpr int NW = kBwdWaves, NBUF = 4, KK = D / 16, DB = D / 32;
   constexpr int kTile = 32 * D * 2;
@@ -207,76 +222,130 @@ void bwd_dq(BwdParams p) {
   u32x4 qf[KK], dof[KK];
   load_operand<D>(p.q + head, q_ld, g, qf);
   load_operand<D>(p.dout + head, q_ld, g, dof);
-  const float lse2 = p.lse[(int64_t)bh * N + q_ld] * kLog2e;
+  const float lse2 = p.lse2[(int64_t)bh * N + q_ld];
   const float di = p.delta[(int64_t)bh * N + q_ld];
   __builtin_amdgcn_sched_barrier(0);
 
   const int n_tiles = (N + 31) / 32;
+  const int n_full = N / 32;
   const int kt_end = CAUSAL ? min(n_tiles, (qt + 1) * (kBwdRows / 32)) : n_tiles;
   const int diag = CAUSAL ? (qt * kBwdRows + wave * 32) / 32 : n_tiles;
   const int my_last = min(diag, n_tiles - 1);
   const int key_lim = CAUSAL ? min(q_row, N - 1) : N - 1;
-  for (int t = 0; t < 3; ++t)
-    if (t < kt_end) {
-      cp.copy(p.k + head, t, N, kbuf(t), wave);
-      cp.copy(p.v + head, t, N, vbuf(t), wave);
-    }
+  // Ring start, virtual steps -3..-1 (K first in each): V0; K0, V1; K1, V2.
+  for (int t = -3; t < 0; ++t) {
+    if (t + 2 >= 0 && t + 2 < kt_end) cp.copy(p.k + head, t + 2, N, kbuf(t + 2), wave);
+    if (t + 3 < kt_end) cp.copy(p.v + head, t + 3, N, vbuf(t + 3), wave);
+  }
 
   f32x16 acc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
 
-  for (int j = 0; j < kt_end; ++j) {
-    const int b = j % NBUF;
-    const bool copies = j + 3 < kt_end;
-    if (copies) {
-      cp.copy(p.k + head, j + 3, N, kbuf((b + 3) % NBUF), wave);
-      cp.copy(p.v + head, j + 3, N, vbuf((b + 3) % NBUF), wave);
-      vm_wait<6 * PER>();  // tiles j+1.. may be in flight; tile j has landed
-    } else {
+  // S^T = K Q^T and dP^T = V dO^T of one tile.
+  auto scores = [&](const char* kt, const char* vt, f32x16& s, f32x16& dp) {
+    s = f32x16{};
+    dp = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      s = Mfma<E>::run(off.read_row(kt, kk), qf[kk], s);
+      dp = Mfma<E>::run(off.read_row(vt, kk), dof[kk], dp);
+    }
+  };
+  // dS^T of one tile, rounded to the element type (hidden keys: exact zeros).
+  auto grad_scores = [&](const f32x16& s, const f32x16& dp, u32x4(&dsf)[2], int key0, bool mask) {
+    float ds[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float pr = exp2_fast(fmaf(s[r], p.c, -lse2));
+      ds[r] = pr * (dp[r] - di);
+      if (mask && key0 + score_key(0, r, g) > key_lim) ds[r] = 0.f;
+    }
+    pack_operand<E>(ds, dsf);
+  };
+  // dQ^T += K^T dS^T of one tile.
+  auto accumulate = [&](const char* kt, const u32x4(&dsf)[2]) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) acc[db] = Mfma<E>::run(off.read_t(kt, db, h), dsf[h], acc[db]);
+  };
+  auto needs_mask = [&](int t) { return t == n_full || (CAUSAL && t == diag); };
+
+  if (kt_end > 2)
+    vm_wait<PER>();
+  else
+    vm_wait<0>();
+  __syncthreads();
+  f32x16 sb[2], dpb[2];
+  u32x4 db_[2][2];
+  scores(kbuf(0), vbuf(0), sb[0], dpb[0]);
+
+  auto step = [&](int t, f32x16& s_cur, f32x16& dp_cur, f32x16& s_nxt, f32x16& dp_nxt, const u32x4(&ds_prev)[2],
+                  u32x4(&ds_cur)[2], auto slot_tag, auto steady_tag) {
+    constexpr bool STEADY = decltype(steady_tag)::value;
+    const int b = STEADY ? decltype(slot_tag)::value : t % NBUF;
+    if (STEADY || t + 2 < kt_end) cp.copy(p.k + head, t + 2, N, kbuf((b + 2) % NBUF), wave);
+    if (STEADY || t + 3 < kt_end) cp.copy(p.v + head, t + 3, N, vbuf((b + 3) % NBUF), wave);
+    if (STEADY || t + 1 <= my_last) scores(kbuf((b + 1) % NBUF), vbuf((b + 1) % NBUF), s_nxt, dp_nxt);
+    if (STEADY || (t >= 1 && t - 1 <= my_last)) accumulate(kbuf((b + 3) % NBUF), ds_prev);
+    if (STEADY || t <= my_last) grad_scores(s_cur, dp_cur, ds_cur, t * 32, !STEADY && needs_mask(t));
+    if (STEADY)
+      vm_wait<PER>();
+    else
       vm_wait<0>();
-    }
     __syncthreads();
-    if (j <= my_last) {
-      const char* kt = kbuf(b);
-      const char* vt = vbuf(b);
-      f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        s = Mfma<E>::run(off.read_row(kt, kk), qf[kk], s);     // S^T = K Q^T
-        dp = Mfma<E>::run(off.read_row(vt, kk), dof[kk], dp);  // dP^T = V dO^T
-      }
-      const int key0 = j * 32;
-      const bool mask = j == n_tiles - 1 || (CAUSAL && j == diag);
-      float ds[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float pr = exp2_fast(fmaf(s[r], p.c, -lse2));
-        const bool hidden = mask && key0 + score_key(0, r, g) > key_lim;
-        ds[r] = hidden ? 0.f : pr * (dp[r] - di);
-      }
-      u32x4 dsf[2];
-      pack_operand<E>(ds, dsf);
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) acc[db] = Mfma<E>::run(off.read_t(kt, db, h), dsf[h], acc[db]);  // dQ^T += K^T dS^T
-    }
-    __syncthreads();  // tile j's slot is rewritten by the copies issued in step j+1
+  };
+  using T = std::true_type;
+  using F = std::false_type;
+  auto rotate = [&]() {
+    sb[0] = sb[1];
+    dpb[0] = dpb[1];
+    db_[1][0] = db_[0][0];
+    db_[1][1] = db_[0][1];
+  };
+  step(0, sb[0], dpb[0], sb[1], dpb[1], db_[1], db_[0], std::integral_constant<int, 0>{}, F{});
+  rotate();
+  int t = 1;
+  // steady groups of four from t = 1 (mod 4): every copy exists and is whole,
+  // every tile lies below every wave's diagonal and needs no mask
+  const int steady_end = CAUSAL ? min(n_full, qt * (kBwdRows / 32)) : n_full;
+#define FA_BWD_STEP(I)                                                                                    \
+  step(t + (I), sb[(I) % 2], dpb[(I) % 2], sb[((I) + 1) % 2], dpb[((I) + 1) % 2], db_[((I) + 1) % 2],     \
+       db_[(I) % 2], std::integral_constant<int, ((I) + 1) % NBUF>{}, T{})
+  for (; t + 6 < kt_end && t + 6 < n_full && t + 4 < steady_end; t += 4) {
+    FA_BWD_STEP(0);
+    FA_BWD_STEP(1);
+    FA_BWD_STEP(2);
+    FA_BWD_STEP(3);
   }
+#undef FA_BWD_STEP
+  for (; t < kt_end; ++t) {
+    step(t, sb[0], dpb[0], sb[1], dpb[1], db_[1], db_[0], std::integral_constant<int, 0>{}, F{});
+    rotate();
+  }
+  if (my_last == kt_end - 1) accumulate(kbuf((kt_end - 1) % NBUF), db_[1]);
   store_rows_t<E, D>(p.dq + head, q_row, N, g, acc, p.scale);
 }
 
 // ---------------------------------------------------------------------------
 // dK, dV: one workgroup per 128 key rows; Q, dO, LSE and D tiles streamed.
+//
+// Query tile u (counted from the workgroup's first, qt_begin) is read as rows
+// for S(u), dP(u) in step u-1, transposed for dV, dK in step u+1, and its
+// statistics in step u. A ring of six slots: step u copies tile u+4 into tile
+// u-2's slot (last read in step u-1); at its end tile u+2 (read in step u+1)
+// must have landed: the copies of steps u-1 and u may still be in flight.
+// One workgroup per CU (the four 32-key waves hold K, V and both
+// accumulators: about 400 registers each), so LDS is plentiful.
 // ---------------------------------------------------------------------------
 template <class E, int D, bool CAUSAL>
 __global__ __launch_bounds__(kBwdWaves * 64) __attribute__((amdgpu_waves_per_eu(1)))
 void bwd_dkdv(BwdParams p) {
-  constexpr int NW = kBwdWaves, NBUF = 4, KK = D / 16, DB = D / 32;
+  constexpr int NW = kBwdWaves, NBUF = 6, KK = D / 16, DB = D / 32;
   constexpr int kTile = 32 * D * 2;
   constexpr int PER = kTile / 1024 / NW;
-  constexpr int kStats = 256;  // 32 LSE floats then 32 D floats
+  constexpr int kStats = 256;  // 32 LSE*log2(e) floats then 32 D floats
   constexpr int kSlot = 2 * kTile + kStats;
   __shared__ __attribute__((aligned(1024))) char smem[NBUF * kSlot];
   auto qbuf = [&](int b) { return smem + b * kSlot; };
@@ -290,16 +359,16 @@ void bwd_dkdv(BwdParams p) {
   const int bh = blk / p.n_tiles, kt = blk % p.n_tiles;
   const int N = p.n;
   const int64_t head = (int64_t)bh * N * D * 2;
-  const float* lse_h = p.lse + (int64_t)bh * N;
+  const float* lse_h = p.lse2 + (int64_t)bh * N;
   const float* del_h = p.delta + (int64_t)bh * N;
 
   TileCopy<D, PER> cp;
   cp.init(wave, lane);
   DualOffsets<D> off;
   off.init(lane);
-  // LSE and D of one 32-query tile: wave 0 copies the 32 LSE values, wave 1
-  // the 32 D values, 4 bytes per lane from lanes 0..31 (rows past N re-read
-  // row N-1: in bounds; those query rows are masked below).
+  // Statistics of one 32-query tile: wave 0 copies the 32 LSE*log2(e) values,
+  // wave 1 the 32 D values, 4 bytes per lane from lanes 0..31 (rows past N
+  // re-read row N-1: in bounds; those query rows are masked below).
   auto copy_stats = [&](int tile, char* dst) {
     if (wave < 2 && lane < 32) {
       const float* src = wave == 0 ? lse_h : del_h;
@@ -308,7 +377,6 @@ void bwd_dkdv(BwdParams p) {
       load_lds4(rs, lds_addr(dst) + wave * 128, min(lane, N - 1 - row0) * 4);
     }
   };
-  const int copies_per_tile = 2 * PER + (wave < 2 ? 1 : 0);
 
   const int key_row = kt * kBwdRows + wave * 32 + l32;
   const int k_ld = min(key_row, N - 1);
@@ -318,83 +386,148 @@ void bwd_dkdv(BwdParams p) {
   __builtin_amdgcn_sched_barrier(0);
 
   const int n_tiles = (N + 31) / 32;
-  // causal: queries before this workgroup's first key see none of its keys
+  const int n_full = N / 32;
+  // causal: queries before this workgroup's first key see none of its keys,
+  // and this wave's keys are first seen by its diagonal query tile
   const int qt_begin = CAUSAL ? min(n_tiles, kt * (kBwdRows / 32)) : 0;
-  const int diag = CAUSAL ? (kt * kBwdRows + wave * 32) / 32 : -1;  // this wave's diagonal query tile
-  auto issue = [&](int t) {
-    const int b = t % NBUF;
-    cp.copy(p.q + head, t, N, qbuf(b), wave);
-    cp.copy(p.dout + head, t, N, dobuf(b), wave);
-    copy_stats(t, stbuf(b));
+  const int diag = CAUSAL ? (kt * kBwdRows + wave * 32) / 32 : 0;
+  const int cnt = n_tiles - qt_begin;
+  const int first = diag - qt_begin;  // first local tile this wave works on
+  auto issue = [&](int u) {
+    const int b = u % NBUF;
+    cp.copy(p.q + head, qt_begin + u, N, qbuf(b), wave);
+    cp.copy(p.dout + head, qt_begin + u, N, dobuf(b), wave);
+    copy_stats(qt_begin + u, stbuf(b));
   };
-  for (int t = qt_begin; t < qt_begin + 3; ++t)
-    if (t < n_tiles) issue(t);
+  for (int u = 0; u < 4; ++u)
+    if (u < cnt) issue(u);
 
   f32x16 dk[DB], dv[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) dk[db] = dv[db] = f32x16{};
 
-  for (int i = qt_begin; i < n_tiles; ++i) {
-    const int b = i % NBUF;
-    const bool copies = i + 3 < n_tiles;
-    if (copies) {
-      issue(i + 3);
-      if (copies_per_tile == 2 * PER + 1)
-        vm_wait<3 * (2 * PER + 1)>();
+  // S = Q K^T and dP = dO V^T of one tile (lane = key, registers = queries).
+  auto scores = [&](int b, f32x16& s, f32x16& dp) {
+    s = f32x16{};
+    dp = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      s = Mfma<E>::run(off.read_row(qbuf(b), kk), kf[kk], s);
+      dp = Mfma<E>::run(off.read_row(dobuf(b), kk), vf[kk], dp);
+    }
+  };
+  // P and dS of one tile, rounded to the element type; hidden pairs (query
+  // past N, or causal query before the key) get exact zeros by selection, so
+  // that padding rows' values never enter a product.
+  auto grad_scores = [&](int b, int u, const f32x16& s, const f32x16& dp, u32x4(&pf)[2], u32x4(&dsf)[2],
+                         bool mask) {
+    const float* st = reinterpret_cast<const float*>(stbuf(b));
+    float pr[16], ds[16];
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      // queries (r/4)*8 + g*4 + r%4 of the tile, r = 4 rr + e
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(st + rr * 8 + g * 4);
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(st + 32 + rr * 8 + g * 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = rr * 4 + e;
+        const float x = exp2_fast(fmaf(s[r], p.c, -l4[e]));
+        pr[r] = x;
+        ds[r] = x * (dp[r] - d4[e]);
+        if (mask) {
+          const int qi = (qt_begin + u) * 32 + score_key(0, r, g);
+          if (qi >= N || (CAUSAL && qi < key_row)) pr[r] = ds[r] = 0.f;
+        }
+      }
+    }
+    pack_operand<E>(pr, pf);
+    pack_operand<E>(ds, dsf);
+  };
+  // dV^T += dO^T P and dK^T += Q^T dS of one tile.
+  auto accumulate = [&](int b, const u32x4(&pf)[2], const u32x4(&dsf)[2]) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        dv[db] = Mfma<E>::run(off.read_t(dobuf(b), db, h), pf[h], dv[db]);
+        dk[db] = Mfma<E>::run(off.read_t(qbuf(b), db, h), dsf[h], dk[db]);
+      }
+  };
+  auto needs_mask = [&](int u) {
+    const int t = qt_begin + u;
+    return t == n_full || (CAUSAL && t == diag);
+  };
+
+  // before step 0: tiles 0 and 1 landed (tiles 2, 3 may still be in flight)
+  if (cnt > 3) {
+    if (wave < 2)
+      vm_wait<2 * (2 * PER + 1)>();
+    else
+      vm_wait<2 * 2 * PER>();
+  } else {
+    vm_wait<0>();
+  }
+  __syncthreads();
+  f32x16 sb[2], dpb[2];
+  u32x4 pb[2][2], db_[2][2];
+  if (0 >= first) scores(0, sb[0], dpb[0]);
+
+  auto step = [&](int u, f32x16& s_cur, f32x16& dp_cur, f32x16& s_nxt, f32x16& dp_nxt, const u32x4(&p_prev)[2],
+                  const u32x4(&ds_prev)[2], u32x4(&p_cur)[2], u32x4(&ds_cur)[2], auto slot_tag, auto steady_tag) {
+    constexpr bool STEADY = decltype(steady_tag)::value;
+    const int b = STEADY ? decltype(slot_tag)::value : u % NBUF;
+    if (STEADY || u + 4 < cnt) issue(u + 4);
+    if (STEADY || (u + 1 < cnt && u + 1 >= first)) scores((b + 1) % NBUF, s_nxt, dp_nxt);
+    if (STEADY || (u >= 1 && u - 1 >= first)) accumulate((b + NBUF - 1) % NBUF, p_prev, ds_prev);
+    if (STEADY || u >= first) grad_scores(b, u, s_cur, dp_cur, p_cur, ds_cur, !STEADY && needs_mask(u));
+    if (STEADY) {
+      if (wave < 2)
+        vm_wait<2 * (2 * PER + 1)>();
       else
-        vm_wait<3 * 2 * PER>();
+        vm_wait<2 * 2 * PER>();
     } else {
       vm_wait<0>();
     }
     __syncthreads();
-    if (!CAUSAL || i >= diag) {
-      const char* qtile = qbuf(b);
-      const char* dot = dobuf(b);
-      const float* st = reinterpret_cast<const float*>(stbuf(b));
-      f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        s = Mfma<E>::run(off.read_row(qtile, kk), kf[kk], s);   // S = Q K^T
-        dp = Mfma<E>::run(off.read_row(dot, kk), vf[kk], dp);   // dP = dO V^T
-      }
-      // LSE and D of this lane's 16 query rows (r/4)*8 + g*4 + r%4
-      float lse2[16], dlt[16];
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const f32x4 a = *reinterpret_cast<const f32x4*>(st + rr * 8 + g * 4);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(st + 32 + rr * 8 + g * 4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          lse2[rr * 4 + e] = a[e] * kLog2e;
-          dlt[rr * 4 + e] = d4[e];
-        }
-      }
-      const int q0 = i * 32;
-      const bool mask = i == n_tiles - 1 || (CAUSAL && i == diag);
-      float pr[16], ds[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int qi = q0 + score_key(0, r, g);
-        const float x = exp2_fast(fmaf(s[r], p.c, -lse2[r]));
-        // hidden pairs get exact zeros (selected, so that padding rows' values
-        // never enter a product)
-        const bool hidden = mask && (qi >= N || (CAUSAL && qi < key_row));
-        pr[r] = hidden ? 0.f : x;
-        ds[r] = hidden ? 0.f : x * (dp[r] - dlt[r]);
-      }
-      u32x4 pf[2], dsf[2];
-      pack_operand<E>(pr, pf);
-      pack_operand<E>(ds, dsf);
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          dv[db] = Mfma<E>::run(off.read_t(dot, db, h), pf[h], dv[db]);     // dV^T += dO^T P
-          dk[db] = Mfma<E>::run(off.read_t(qtile, db, h), dsf[h], dk[db]);  // dK^T += Q^T dS
-        }
-    }
-    __syncthreads();  // tile i's slot is rewritten by the copies issued in step i+1
+  };
+  using T = std::true_type;
+  using F = std::false_type;
+  auto rotate = [&]() {
+    sb[0] = sb[1];
+    dpb[0] = dpb[1];
+    pb[1][0] = pb[0][0];
+    pb[1][1] = pb[0][1];
+    db_[1][0] = db_[0][0];
+    db_[1][1] = db_[0][1];
+  };
+  int u = 0;
+  // run-time steps until a steady group can start: u = 1 (mod 6) and (causal)
+  // past every wave's diagonal tile (local tile 3)
+  const int steady_from = CAUSAL ? 7 : 1;
+  for (; u < cnt && u < steady_from; ++u) {
+    step(u, sb[0], dpb[0], sb[1], dpb[1], pb[1], db_[1], pb[0], db_[0], std::integral_constant<int, 0>{}, F{});
+    rotate();
   }
+  // steady groups of six: every copy exists and is whole, no mask
+#define FA_BWD_STEP(I)                                                                                          \
+  step(u + (I), sb[(I) % 2], dpb[(I) % 2], sb[((I) + 1) % 2], dpb[((I) + 1) % 2], pb[((I) + 1) % 2],            \
+       db_[((I) + 1) % 2], pb[(I) % 2], db_[(I) % 2], std::integral_constant<int, ((I) + 1) % NBUF>{}, T{})
+  if (u == steady_from) {
+    for (; u + 9 < cnt && qt_begin + u + 9 < n_full; u += 6) {
+      FA_BWD_STEP(0);
+      FA_BWD_STEP(1);
+      FA_BWD_STEP(2);
+      FA_BWD_STEP(3);
+      FA_BWD_STEP(4);
+      FA_BWD_STEP(5);
+    }
+  }
+#undef FA_BWD_STEP
+  for (; u < cnt; ++u) {
+    step(u, sb[0], dpb[0], sb[1], dpb[1], pb[1], db_[1], pb[0], db_[0], std::integral_constant<int, 0>{}, F{});
+    rotate();
+  }
+  if (cnt >= 1 && cnt - 1 >= first) accumulate((cnt - 1) % NBUF, pb[1], db_[1]);
   store_rows_t<E, D>(p.dk + head, key_row, N, g, dk, p.scale);
   store_rows_t<E, D>(p.dv + head, key_row, N, g, dv, 1.f);
 }
@@ -418,6 +551,7 @@ hipError_t run_bwd(const BwdArgs& a) {
   p.c = a.scale * kLog2e;
   p.scale = a.scale;
   const int64_t rows = (int64_t)a.B * a.H * a.N;
+  p.lse2 = a.delta + rows;
   constexpr int kRowsPerBlock = 4 * (64 / (D / 8));
   hipLaunchKernelGGL((bwd_delta<E, D>), dim3((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock)), dim3(256), 0,
                      a.stream, p, rows);
