@@ -23,10 +23,12 @@
 //    dV^T += dO^T P and dK^T += Q^T dS, with dO^T and Q^T read transposed.
 // Streamed tiles travel global -> LDS directly (buffer_load ... lds) through
 // rings of LDS slots; tiles read both as rows and transposed use the `dual`
-// chunk swizzle. Both kernels are software pipelined: in step t the matrix
-// cores form S and dP of tile t+1 and add the gradient products of tile t-1,
-// while the vector ALUs turn tile t's S and dP into P and dS. No work of a
-// step waits on a product issued in the same step.
+// chunk swizzle. Both kernels are software pipelined. In bwd_dkdv's step t
+// the matrix cores form S and dP of tile t+1 and add the gradient products
+// of tile t-1, while the vector ALUs turn tile t's S and dP into P and dS;
+// no work of a step waits on a product issued in the same step. bwd_dq forms
+// tile t's S and dP first and covers their latency with tile t-1's dQ
+// product (fewer live registers: two waves per SIMD also for causal).
 #include "fa_device.h"
 #include "fa_launch.h"
 
@@ -187,14 +189,16 @@ __device__ __forceinline__ void store_rows_t(char* head, int row, int n, int g, 
 // ---------------------------------------------------------------------------
 // dQ: one workgroup per 128 query rows; K and V tiles streamed.
 //
-// K tile t is read twice: as rows for S(t) in step t-1 and transposed for
-// dQ += K^T dS(t) in step t+1; V tile t once, for dP(t) in step t-1. Step t
-// copies K_{t+2} into K_{t-2}'s slot (last read in step t-1) and V_{t+3} into
-// V_{t-1}'s (last read in step t-2); at its end K_{t+2} and V_{t+2} (read in
-// step t+1) must have landed: at most this step's V copies may be in flight.
+// Step t forms S^T and dP^T of tile t, then adds the dQ product of tile t-1
+// (independent of them, it covers their latency), then turns tile t's scores
+// into dS. K tile t is read as rows in step t and transposed in step t+1; V
+// tile t as rows in step t. Step t copies K_{t+2} into K_{t-2}'s slot (last
+// read in step t-1) and V_{t+3} into V_{t-1}'s (last read in step t-1); at
+// its end K_{t+1} and V_{t+1} must have landed: this step's copies may still
+// be in flight.
 // ---------------------------------------------------------------------------
 template <class E, int D, bool CAUSAL>
-__global__ __launch_bounds__(kBwdWaves * 64) __attribute__((amdgpu_waves_per_eu(CAUSAL && D == 128 ? 1 : 2)))
+__global__ __launch_bounds__(kBwdWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void bwd_dq(BwdParams p) {
   constexpr int NW = kBwdWaves, NBUF = 4, KK = D / 16, DB = D / 32;
   constexpr int kTile = 32 * D * 2;
@@ -272,48 +276,47 @@ void bwd_dq(BwdParams p) {
   };
   auto needs_mask = [&](int t) { return t == n_full || (CAUSAL && t == diag); };
 
+  // before step 0: K0 and V0 landed (V1, K1, V2 may be in flight)
   if (kt_end > 2)
-    vm_wait<PER>();
+    vm_wait<3 * PER>();
   else
     vm_wait<0>();
   __syncthreads();
-  f32x16 sb[2], dpb[2];
   u32x4 db_[2][2];
-  scores(kbuf(0), vbuf(0), sb[0], dpb[0]);
 
-  auto step = [&](int t, f32x16& s_cur, f32x16& dp_cur, f32x16& s_nxt, f32x16& dp_nxt, const u32x4(&ds_prev)[2],
-                  u32x4(&ds_cur)[2], auto slot_tag, auto steady_tag) {
+  auto step = [&](int t, const u32x4(&ds_prev)[2], u32x4(&ds_cur)[2], auto slot_tag, auto steady_tag) {
     constexpr bool STEADY = decltype(steady_tag)::value;
     const int b = STEADY ? decltype(slot_tag)::value : t % NBUF;
     if (STEADY || t + 2 < kt_end) cp.copy(p.k + head, t + 2, N, kbuf((b + 2) % NBUF), wave);
     if (STEADY || t + 3 < kt_end) cp.copy(p.v + head, t + 3, N, vbuf((b + 3) % NBUF), wave);
-    if (STEADY || t + 1 <= my_last) scores(kbuf((b + 1) % NBUF), vbuf((b + 1) % NBUF), s_nxt, dp_nxt);
+    f32x16 s, dp;
+    if (STEADY || t <= my_last) scores(kbuf(b), vbuf(b), s, dp);
     if (STEADY || (t >= 1 && t - 1 <= my_last)) accumulate(kbuf((b + 3) % NBUF), ds_prev);
-    if (STEADY || t <= my_last) grad_scores(s_cur, dp_cur, ds_cur, t * 32, !STEADY && needs_mask(t));
+    if (STEADY || t <= my_last) grad_scores(s, dp, ds_cur, t * 32, !STEADY && needs_mask(t));
     if (STEADY)
-      vm_wait<PER>();
+      vm_wait<2 * PER>();
     else
       vm_wait<0>();
     __syncthreads();
   };
   using T = std::true_type;
   using F = std::false_type;
-  auto rotate = [&]() {
-    sb[0] = sb[1];
-    dpb[0] = dpb[1];
-    db_[1][0] = db_[0][0];
-    db_[1][1] = db_[0][1];
-  };
-  step(0, sb[0], dpb[0], sb[1], dpb[1], db_[1], db_[0], std::integral_constant<int, 0>{}, F{});
-  rotate();
-  int t = 1;
-  // steady groups of four from t = 1 (mod 4): every copy exists and is whole,
+  int t = 0;
+  // steady groups of four from t = 0 (mod 4): every copy exists and is whole,
   // every tile lies below every wave's diagonal and needs no mask
   const int steady_end = CAUSAL ? min(n_full, qt * (kBwdRows / 32)) : n_full;
-#define FA_BWD_STEP(I)                                                                                    \
-  step(t + (I), sb[(I) % 2], dpb[(I) % 2], sb[((I) + 1) % 2], dpb[((I) + 1) % 2], db_[((I) + 1) % 2],     \
-       db_[(I) % 2], std::integral_constant<int, ((I) + 1) % NBUF>{}, T{})
-  for (; t + 6 < kt_end && t + 6 < n_full && t + 4 < steady_end; t += 4) {
+#define FA_BWD_STEP(I) step(t + (I), db_[((I) + 1) % 2], db_[(I) % 2], std::integral_constant<int, (I) % NBUF>{}, T{})
+  // step 0 has no previous tile: run it at run time
+  step(0, db_[1], db_[0], std::integral_constant<int, 0>{}, F{});
+  db_[1][0] = db_[0][0];
+  db_[1][1] = db_[0][1];
+  t = 1;
+  for (; t < kt_end && (t % 4) != 0; ++t) {
+    step(t, db_[1], db_[0], std::integral_constant<int, 0>{}, F{});
+    db_[1][0] = db_[0][0];
+    db_[1][1] = db_[0][1];
+  }
+  for (; t + 6 < kt_end && t + 6 < n_full && t + 3 < steady_end; t += 4) {
     FA_BWD_STEP(0);
     FA_BWD_STEP(1);
     FA_BWD_STEP(2);
@@ -321,8 +324,9 @@ void bwd_dq(BwdParams p) {
   }
 #undef FA_BWD_STEP
   for (; t < kt_end; ++t) {
-    step(t, sb[0], dpb[0], sb[1], dpb[1], db_[1], db_[0], std::integral_constant<int, 0>{}, F{});
-    rotate();
+    step(t, db_[1], db_[0], std::integral_constant<int, 0>{}, F{});
+    db_[1][0] = db_[0][0];
+    db_[1][1] = db_[0][1];
   }
   if (my_last == kt_end - 1) accumulate(kbuf((kt_end - 1) % NBUF), db_[1]);
   store_rows_t<E, D>(p.dq + head, q_row, N, g, acc, p.scale);
