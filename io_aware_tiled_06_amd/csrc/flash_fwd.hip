@@ -109,11 +109,12 @@ __device__ __forceinline__ bool update_max(float m_tile, float& m_run, float& l_
 // ---------------------------------------------------------------------------
 // Half-precision inputs (bf16 / fp16): matrix cores, float32 accumulation.
 //
-// A workgroup of NW waves owns NW * 32 query rows; key tiles of BC = 32. Two
-// workgroups share a CU, so every SIMD runs two waves of independent
-// workgroups. (Two 32-row blocks per wave would halve the LDS reads per
-// product but needs about 460 registers per lane, hence one wave per SIMD;
-// measured slower on MI355X, as was an 8-wave workgroup.)
+// A workgroup of NW waves owns NW * 32 query rows; key tiles of BC = 32.
+// Every SIMD runs two waves: of two 4-wave workgroups per CU, or of one
+// 8-wave workgroup (used on large grids: each K/V tile is then copied into
+// LDS once for 256 query rows instead of 128). (Two 32-row blocks per wave
+// would halve the LDS reads per product but needs about 460 registers per
+// lane, hence one wave per SIMD; measured slower on MI355X.)
 //
 // Software pipeline, step t: the matrix cores form the scores of tile t+1 and
 // add P_{t-1} V_{t-1} into the accumulator; the vector ALUs turn tile t's
@@ -661,6 +662,26 @@ hipError_t run_half(const AttnArgs& a) {
       hipLaunchKernelGGL((flash_fwd_half<E, D, kWavesHalf, 2, false, CAUSAL>), dim3(p.n_blocks),
                          dim3(kWavesHalf * 64 * 2), 0, a.stream, p);
     return hipGetLastError();
+  }
+  // Large grids at d = 128: workgroups of 8 waves (256 query rows, one per
+  // CU) copy each K/V tile once for twice the rows, halving the copy traffic
+  // into LDS. Only with at least four full rounds of them, so that a partial
+  // last round stays a small share (with fewer, measured slower).
+  if constexpr (D == 128) {
+    constexpr int kWide = 2 * kWavesHalf;
+    const int nq = (a.N + kWide * 32 - 1) / (kWide * 32);
+    const int nb = a.B * a.H * nq;
+    if (nb >= 4 * device_cus()) {
+      p.n_qtiles = nq;
+      p.n_blocks = nb;
+      if (a.scale < 0.f)
+        hipLaunchKernelGGL((flash_fwd_half<E, D, kWide, 1, true, CAUSAL>), dim3(nb), dim3(kWide * 64), 0,
+                           a.stream, p);
+      else
+        hipLaunchKernelGGL((flash_fwd_half<E, D, kWide, 1, false, CAUSAL>), dim3(nb), dim3(kWide * 64), 0,
+                           a.stream, p);
+      return hipGetLastError();
+    }
   }
   if (a.scale < 0.f)
     hipLaunchKernelGGL((flash_fwd_half<E, D, kWavesHalf, 1, true, CAUSAL>), dim3(p.n_blocks),
