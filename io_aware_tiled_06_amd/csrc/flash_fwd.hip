@@ -430,7 +430,13 @@ void flash_fwd_half(FwdParams p) {
     FA_STEADY_STEP(3);
   }
 #undef FA_STEADY_STEP
-  for (; t < steps; ++t) {
+  // remaining steps in pairs with the buffers' roles swapped (no register
+  // moves), then at most one more
+  for (; t + 1 < steps; t += 2) {
+    step(t, sb[0], sb[1], pb[1], pb[0], std::integral_constant<int, 0>{}, F{});
+    step(t + 1, sb[1], sb[0], pb[0], pb[1], std::integral_constant<int, 0>{}, F{});
+  }
+  if (t < steps) {
     step(t, sb[0], sb[1], pb[1], pb[0], std::integral_constant<int, 0>{}, F{});
     rotate();
   }
@@ -663,15 +669,17 @@ hipError_t run_half(const AttnArgs& a) {
                          dim3(kWavesHalf * 64 * 2), 0, a.stream, p);
     return hipGetLastError();
   }
-  // Large grids at d = 128: workgroups of 8 waves (256 query rows, one per
-  // CU) copy each K/V tile once for twice the rows, halving the copy traffic
-  // into LDS. Only with at least four full rounds of them, so that a partial
-  // last round stays a small share (with fewer, measured slower).
+  // Long sequences on large grids at d = 128: workgroups of 8 waves (256
+  // query rows, one per CU) copy each K/V tile once for twice the rows,
+  // halving the copy traffic into LDS and the K/V re-reads from L2. Only for
+  // N >= 8192 (shorter heads pad a 256-row tile or run too few steps to gain:
+  // measured slower from N = 16 to 1024) and with at least four full rounds of
+  // workgroups, so that a partial last round stays a small share.
   if constexpr (D == 128) {
     constexpr int kWide = 2 * kWavesHalf;
     const int nq = (a.N + kWide * 32 - 1) / (kWide * 32);
     const int nb = a.B * a.H * nq;
-    if (nb >= 4 * device_cus()) {
+    if (a.N >= 8192 && nb >= 4 * device_cus()) {
       p.n_qtiles = nq;
       p.n_blocks = nb;
       if (a.scale < 0.f)
