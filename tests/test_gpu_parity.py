@@ -299,6 +299,28 @@ def test_causal_long_context_sampled_rows(long_context):
     assert torch.equal(o[:, :, 0], tv[:, :, 0])
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_wide_workgroups_ragged_sampled_rows(causal):
+    """A grid that takes the 8-wave, 256-row workgroups (N >= 8192 and at
+    least four rounds of them: B=2, H=16, N=8200 gives 1056) with a ragged
+    last key and query tile (8200 = 256*32 + 8); sampled rows, including the
+    last ones and those around tile edges, against the oracle."""
+    w = Workload("wide", 2, 16, 8200, 128, "bf16", 77, 3.0)
+    q, k, v = make_inputs(w)
+    tq, tk, tv = dev(q, w.dtype), dev(k, w.dtype), dev(v, w.dtype)
+    print(f"[parity] wide workgroups N=8200 causal={causal}", flush=True)
+    o, lse = fa.flash_attn_fwd(tq, tk, tv, w.scale, causal=causal)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([sample_rows(w.N, 24), [0, 31, 32, 255, 256, 8191, 8192, 8195, 8199]]))
+    o_s = o[:, :, rows].float().cpu().numpy().astype(np.float64)
+    lse_s = lse[:, :, rows].cpu().numpy().astype(np.float64)
+    if causal:
+        o_ref, lse_ref = causal_rows_reference(q, k, v, w.scale, rows)
+    else:
+        o_ref, lse_ref = attention_reference(q[:, :, rows], k, v, w.scale)
+    assert_close(o_s, lse_s, o_ref, lse_ref, w.dtype, f"wide N=8200 causal={causal}")
+
+
 @pytest.mark.parametrize("dtype", ["fp32", "fp16", "bf16"])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("n", EDGE_N + [300, 1000])
