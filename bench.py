@@ -99,10 +99,18 @@ def cpu_baseline(w, q, k, v, target_s: float = 15.0):
     t = time.perf_counter() - t0
     rows = n_heads * w.N + rows_last
     flops = 4.0 * rows * w.N * w.d
+    cpu = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), None)
+    except OSError:
+        pass
     return {
         "value": round(flops / t / 1e12, 6),
         "unit": "TFLOP/s",
         "cores": int(threads),
+        "cpu_model": cpu,
+        "seconds": round(t, 2),
         "kind": "oracle",
         "sample": (f"{n_heads} whole head(s) + {rows_last} query rows of the next, each row against all "
                    f"{w.N} keys ({rows} rows of {w.B * w.H * w.N}), float64 numpy; {t:.2f} s"),
@@ -275,7 +283,7 @@ def main() -> int:
         crossover_sweep()
         return 0
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path",
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the library has no multi-GPU path",
               file=sys.stderr)
         return 2
 
@@ -376,6 +384,8 @@ def main() -> int:
                                  else traffic.compulsory_bytes(w.B, w.H, w.N, w.d, w.elem_bytes)),
         },
         "device": torch.cuda.get_device_name(dev),
+        "device_cus": torch.cuda.get_device_properties(dev).multi_processor_count,
+        "peak_formula": "256 CUs x 2.4 GHz x 4096 FLOP/clk/CU (dense bf16/fp16 matrix cores); fp32: 157.3 TFLOP/s",
     }
     if args.backward:
         line["roofline"]["kernels"] = "bwd_delta + bwd_dq + bwd_dkdv (one backward pass)"
