@@ -276,11 +276,11 @@ void bwd_dq(BwdParams p) {
   };
   auto needs_mask = [&](int t) { return t == n_full || (CAUSAL && t == diag); };
 
-  // before step 0: K0 and V0 landed (V1, K1, V2 may be in flight)
-  if (kt_end > 2)
-    vm_wait<3 * PER>();
-  else
-    vm_wait<0>();
+  // Before step 0: the query-side operands and statistics and every prologue
+  // copy have landed. A wait the compiler sees: it then puts none of its own
+  // in front of the loop's uses of qf, dof, lse2 and di, which would also
+  // count (one in-order counter) the K/V copies a step has just issued.
+  wait_vmem_all();
   __syncthreads();
   u32x4 db_[2][2];
 
@@ -462,15 +462,11 @@ void bwd_dkdv(BwdParams p) {
     return t == n_full || (CAUSAL && t == diag);
   };
 
-  // before step 0: tiles 0 and 1 landed (tiles 2, 3 may still be in flight)
-  if (cnt > 3) {
-    if (wave < 2)
-      vm_wait<2 * (2 * PER + 1)>();
-    else
-      vm_wait<2 * 2 * PER>();
-  } else {
-    vm_wait<0>();
-  }
+  // Before step 0: kf, vf and every prologue copy have landed. A wait the
+  // compiler sees, so that it puts none of its own in front of the loop's
+  // uses of kf and vf (such a wait would also count the copies a step has
+  // just issued).
+  wait_vmem_all();
   __syncthreads();
   f32x16 sb[2], dpb[2];
   u32x4 pb[2][2], db_[2][2];

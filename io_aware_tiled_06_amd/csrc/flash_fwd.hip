@@ -35,6 +35,16 @@ namespace fa {
 namespace {
 
 constexpr float kLazyRescale = 8.0f;  // log2 units
+// Operands of the next step's products read one step early: the first
+// FA_FWD_KP K operands of the score product and the first FA_FWD_VP V^T
+// operands of the P V product (tunable at build time; at d = 128 these
+// values keep every variant within 256 registers without spills).
+#ifndef FA_FWD_VP
+#define FA_FWD_VP 4
+#endif
+#ifndef FA_FWD_KP
+#define FA_FWD_KP 2
+#endif
 
 struct FwdParams {
   const char* q;
@@ -123,9 +133,10 @@ __device__ __forceinline__ bool update_max(float m_tile, float& m_run, float& l_
 // the same step, so each wave's matrix and vector work can overlap freely and
 // the two waves of a SIMD fill each other's gaps. K tiles are copied four
 // tiles ahead and V tiles two (rings of four slots each; a slot is rewritten
-// only after the barrier that follows its last read). The first two K
-// operands of the next step's score product are read from LDS during the
-// current step, so the matrix cores start each step without waiting on LDS.
+// only after the barrier that follows its last read). The first K operands
+// of the next step's score product and the first V^T operands of its P V
+// product are read from LDS during the current step, so the matrix cores
+// start each step without waiting on LDS.
 //
 // Running maximum: tile t's probabilities are first computed with m as it
 // stands. If every lane's sum of its 16 probabilities is at most 2^8, every
@@ -280,7 +291,7 @@ void flash_fwd_half(FwdParams p) {
 
   // S^T = K Q^T for one tile (32 keys x 32 queries); its first KP operands
   // were read one step earlier (prefetch_k).
-  constexpr int KP = 2;
+  constexpr int KP = FA_FWD_KP;
   u32x4 pre_k[KP];
   auto prefetch_k = [&](const char* kb_lds) {
 #pragma unroll
@@ -318,15 +329,29 @@ void flash_fwd_half(FwdParams p) {
       }
     return ls[0] + ls[1];
   };
+  // V^T operand (feature block db, key half h) of a tile, two transposing reads.
+  auto read_vt = [&](const char* vb_lds, int db, int h) {
+    const char* a = vb_lds + v_off[db] + h * 16 * RB;
+    const u32x2 lo = lds_read_tr16(a), hi = lds_read_tr16(a + 8 * RB);
+    return u32x4{lo[0], lo[1], hi[0], hi[1]};
+  };
+  // The first VP operands of the next step's P V product, read during the
+  // current step: that step's first products then need no LDS round trip
+  // right after the barrier, when both waves of a SIMD would wait on it.
+  constexpr int VP = FA_FWD_VP;
+  u32x4 pre_v[VP > 0 ? VP : 1];
+  auto prefetch_v = [&](const char* vb_lds) {
+#pragma unroll
+    for (int i = 0; i < VP; ++i) pre_v[i] = read_vt(vb_lds, i / 2, i % 2);
+  };
   // O^T += V^T P^T for one tile.
   auto accumulate = [&](const char* vb_lds, const u32x4(&pf)[2]) {
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const char* a = vb_lds + v_off[db] + h * 16 * RB;
-        const u32x2 lo = lds_read_tr16(a), hi = lds_read_tr16(a + 8 * RB);
-        const u32x4 vt = {lo[0], lo[1], hi[0], hi[1]};
+        const int i = db * 2 + h;
+        const u32x4 vt = i < VP ? pre_v[i < VP ? i : 0] : read_vt(vb_lds, db, h);
         acc[db] = Mfma<E>::run(vt, pf[h], acc[db]);
       }
   };
@@ -359,13 +384,13 @@ void flash_fwd_half(FwdParams p) {
   // Tiles that need masking: the ragged last one, and (causal) the diagonal.
   auto needs_mask = [&](int t) { return kt0 + t == n_full || (CAUSAL && kt0 + t == diag); };
 
-  // K0, K1, K2 and V0 have landed once at most the copies K3, V1 are in
-  // flight (vector-memory operations complete in issue order); with fewer
-  // than four tiles, wait for everything.
-  if (cnt > 3)
-    vm_wait<2 * kPer>();
-  else
-    vm_wait<0>();
+  // Wait for the query loads and every prologue copy. The wait is one the
+  // compiler sees (it does not see the copies): it then knows the query
+  // fragments are in registers on every path into the loop, and puts no wait
+  // of its own in front of the loop's score products. Such a wait would
+  // count this step's K/V copies too (one in-order counter) and make every
+  // step wait for the copies it has just issued.
+  wait_vmem_all();
   __syncthreads();
   f32x16 sb[2];
   u32x4 pb[2][2];
@@ -398,6 +423,7 @@ void flash_fwd_half(FwdParams p) {
     if (STEADY || t + 1 <= last) scores(kbuf((b + 1) % NBUF), s_nxt);
     if (STEADY || (t >= 1 && t - 1 <= last)) accumulate(vbuf((b + 3) % NBUF), p_prev);
     prefetch_k(kbuf((b + 2) % NBUF));  // stale (unused) past the last tile
+    prefetch_v(vbuf(b));               // V_t, landed before this step began
     if (STEADY || t <= last) softmax_tile(s_cur, p_cur, (kt0 + t) * BC, !STEADY && needs_mask(t));
     if (STEADY)
       vm_wait<2 * kPer>();
