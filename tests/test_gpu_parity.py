@@ -359,3 +359,44 @@ def test_causal_deterministic_and_independent_of_future():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
     assert torch.equal(o1[:, :, :1500], o3[:, :, :1500]) and torch.equal(l1[:, :, :1500], l3[:, :, :1500])
     assert not torch.equal(o1[:, :, 1500:], o3[:, :, 1500:])
+
+
+# -- every launch shape of the half-precision kernel ------------------------------
+
+# Grids chosen so that, on a 256-CU MI355X, each takes one launch shape of the
+# float16/bfloat16 forward pass:
+#   split   72 query tiles (< 2 per CU): 8-wave workgroups, keys split over two groups
+#   rounds  1024 tiles, N < 8192: 4-wave workgroups, whole rounds only
+#   rest    630 tiles: two whole rounds of 4-wave workgroups, then 118 tiles
+#           with the key split (non-causal; causal runs them in one launch)
+#   wide    N >= 8192 and 1056 tiles of 256 rows: 8-wave, 256-row workgroups
+# All lengths are ragged in the 32-key and the query tiles.
+LAUNCH_SHAPES = {"split": (1, 3, 2999), "rounds": (1, 16, 8100), "rest": (1, 10, 7999), "wide": (2, 16, 8200)}
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("shape", list(LAUNCH_SHAPES))
+def test_launch_shapes_both_signs_sampled_rows(shape, dtype):
+    """Each launch shape, both element types, a positive and a negative scale
+    (the kernel is instantiated per sign of the scale), causal and not:
+    sampled rows, including tile edges and the last rows, against the oracle."""
+    B, H, N = LAUNCH_SHAPES[shape]
+    w = Workload(f"shape-{shape}", B, H, N, 128, dtype, 90 + N % 7, 2.0)
+    q, k, v = make_inputs(w)
+    tq, tk, tv = dev(q, dtype), dev(k, dtype), dev(v, dtype)
+    edges = [0, 31, 32, 127, 128, 255, 256, N - 33, N - 32, N - 2, N - 1]
+    rows = np.unique(np.concatenate([sample_rows(N, 16), [r for r in edges if 0 <= r < N]]))
+    for scale in (w.scale, -0.6 * w.scale):
+        s = float(np.float32(scale))
+        for causal in (False, True):
+            what = f"{shape} B{B} H{H} N{N} {dtype} scale={s:+.4f} causal={causal}"
+            print(f"[parity] {what}", flush=True)
+            o, lse = fa.flash_attn_fwd(tq, tk, tv, s, causal=causal)
+            torch.cuda.synchronize()
+            o_s = o[:, :, rows].float().cpu().numpy().astype(np.float64)
+            lse_s = lse[:, :, rows].cpu().numpy().astype(np.float64)
+            if causal:
+                o_ref, lse_ref = causal_rows_reference(q, k, v, s, rows)
+            else:
+                o_ref, lse_ref = attention_reference(q[:, :, rows], k, v, s)
+            assert_close(o_s, lse_s, o_ref, lse_ref, dtype, what)
