@@ -31,9 +31,11 @@
  * screened: they propagate into the outputs.
  *
  * Streams: `stream` is a hipStream_t passed as void*; NULL selects the null
- * stream. Calls are asynchronous on that stream and never synchronise.
- * The library holds no per-call state, so calls from several host threads
- * are safe.
+ * stream. Kernels are launched on the calling thread's current HIP device,
+ * and `stream` must belong to that device. Calls are asynchronous on that
+ * stream and never synchronise. The library holds no per-call state (only a
+ * per-device cache of the compute-unit count, read on first use), so calls
+ * from several host threads are safe.
  */
 #ifndef FLASH_ATTN_H
 #define FLASH_ATTN_H

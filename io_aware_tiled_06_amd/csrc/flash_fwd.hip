@@ -25,6 +25,7 @@
 //    result is the same in exact arithmetic because numerator and denominator
 //    share the same m.
 //  * Workgroup ids are remapped so that each XCD works on contiguous heads.
+#include <atomic>
 #include <type_traits>
 
 #include "fa_device.h"
@@ -662,15 +663,17 @@ constexpr int kWavesF32 = 4;
 
 // Compute units of the current device (cached per device).
 int device_cus() {
-  static int cus[64] = {};
+  // Per-device cache; concurrent first calls from several host threads store
+  // the same value, so relaxed atomics suffice.
+  static std::atomic<int> cus[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cus[dev] == 0) {
-    int n = 0;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cus[dev] = n;
+    cus[dev].store(n, std::memory_order_relaxed);
   }
-  return cus[dev];
+  return n;
 }
 
 template <class E, int D, bool CAUSAL>
