@@ -380,6 +380,7 @@ def main() -> int:
             "traffic": hbm,
             "kernel_ms": round(kern_ms, 4),
             "kernel_ms_min": round(float(np.min(ev_ms)), 4),
+            "kernel_ms_median": round(float(np.median(ev_ms)), 4),
             "compulsory_bytes": (bwd_compulsory_bytes(w) if args.backward
                                  else traffic.compulsory_bytes(w.B, w.H, w.N, w.d, w.elem_bytes)),
         },
