@@ -108,15 +108,16 @@ int flash_attn_fwd_causal(const void* q, const void* k, const void* v, void* o, 
  * nothing N x N is written.
  *
  * Arguments: q, k, v, o, dout, dq, dk, dv: [B,H,N,d] device pointers of
- * `dtype` (FA_F16 or FA_BF16; FA_F32 returns FA_ERR_UNSUPPORTED); lse: the
+ * `dtype` (FA_F32, FA_F16 or FA_BF16); lse: the
  * [B,H,N] float32 output of the forward pass with the same inputs and scale;
  * delta: caller-owned float32 scratch of 2*B*H*N elements, overwritten with
  * D ([B,H,N], first half) and LSE*log2(e) ([B,H,N], second half); the
  * library allocates nothing. All 16-byte aligned; outputs must not alias
  * inputs. Three kernels run in order on `stream`. Arithmetic: products on the
- * matrix cores with float32 accumulation, P and dS rounded to the input type
- * before their products, gradients rounded to nearest even. Deterministic
- * (no atomics). Validation and status codes as flash_attn_fwd (d in {64,128}).
+ * matrix cores with float32 accumulation; for FA_F16/FA_BF16, P and dS are
+ * rounded to the input type before their products and the gradients to
+ * nearest even; for FA_F32 every step is float32. Deterministic (no
+ * atomics). Validation and status codes as flash_attn_fwd (d in {64,128}).
  */
 int flash_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
                    const float* lse, void* dq, void* dk, void* dv, float* delta,

@@ -169,8 +169,8 @@ def flash_attn_bwd(q, k, v, o, lse, dout, scale=None, *, causal=False, dq=None, 
                    stream=None):
     """Gradients of the fused forward pass (dQ, dK, dV) on the GPU.
 
-    q, k, v, o, dout: contiguous [B, H, N, d] float16/bfloat16 tensors on one
-    GPU; lse: the float32 [B, H, N] LSE that flash_attn_fwd returned for these
+    q, k, v, o, dout: contiguous [B, H, N, d] float32, float16 or bfloat16
+    tensors on one GPU; lse: the float32 [B, H, N] LSE that flash_attn_fwd returned for these
     inputs (and the same `causal`). dq, dk, dv default to new tensors like q;
     delta (float32 scratch of 2 * B * H * N elements) to a new tensor. Returns
     (dq, dk, dv).

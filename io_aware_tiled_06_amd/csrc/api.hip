@@ -87,7 +87,6 @@ static int flash_attn_bwd_impl(const void* q, const void* k, const void* v, cons
   bool empty;
   const int st = validate(q, k, v, dq, lse, B, H, N, d, scale, dtype, &empty);
   if (st != FA_OK || empty) return st;
-  if (dtype == FA_F32) return FA_ERR_UNSUPPORTED;
   if (!o || !dout || !lse || !dk || !dv || !delta) return FA_ERR_NULL;
   if (!aligned16(o) || !aligned16(dout) || !aligned16(dk) || !aligned16(dv) || !aligned16(delta))
     return FA_ERR_ALIGN;

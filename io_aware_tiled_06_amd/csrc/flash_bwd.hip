@@ -532,8 +532,281 @@ void bwd_dkdv(BwdParams p) {
   store_rows_t<E, D>(p.dv + head, key_row, N, g, dv, 1.f);
 }
 
-template <class E, int D, bool CAUSAL>
-hipError_t run_bwd(const BwdArgs& a) {
+// ---------------------------------------------------------------------------
+// float32 inputs: the same three steps with every value in float32, products
+// on the float32 matrix cores (32x32x2: lane l supplies A[l%32][l/32] and
+// B[l/32][l%32], one element each). Tiles are staged through registers into
+// two LDS buffers, as in the float32 forward pass; one wave per SIMD.
+//
+// Feature pairing of the score products: product 4i + e contracts features
+// 8i + e (lane group 0) and 8i + 4 + e (lane group 1) of both operands.
+// Products over a 32-row tile pair rows score_key(0, r, g) of lane group g
+// for register r, so a score register is directly the B operand.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void bwd_delta_f32(BwdParams p, int64_t rows) {
+  constexpr int LPR = D / 4;     // lanes per row, 4 floats each
+  constexpr int RPW = 64 / LPR;  // rows per wave
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t row = ((int64_t)blockIdx.x * 4 + wave) * RPW + lane / LPR;
+  float acc = 0.f;
+  if (row < rows) {
+    const int64_t off = (row * D + (lane % LPR) * 4) * 4;
+    const f32x4 a = __builtin_bit_cast(f32x4, ld_global16(p.o + off));
+    const f32x4 b = __builtin_bit_cast(f32x4, ld_global16(p.dout + off));
+    acc = a[0] * b[0] + a[1] * b[1] + a[2] * b[2] + a[3] * b[3];
+  }
+#pragma unroll
+  for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+  if (row < rows && lane % LPR == 0) {
+    p.delta[row] = acc;
+    p.lse2[row] = p.lse[row] * kLog2e;
+  }
+}
+
+// Features 8i + 4g + e (e = 0..3) of row `row`: the operand of products 4i + e.
+template <int D>
+__device__ __forceinline__ void load_operand_f32(const char* head, int row, int g, f32x4 (&f)[D / 8]) {
+#pragma unroll
+  for (int i = 0; i < D / 8; ++i)
+    f[i] = __builtin_bit_cast(f32x4, ld_global16(head + ((int64_t)row * D + i * 8 + g * 4) * 4));
+}
+
+template <int D>
+__device__ __forceinline__ void store_rows_f32(char* head, int row, int n, int g, const f32x16 (&acc)[D / 32],
+                                               float mul) {
+  if (row >= n) return;
+  char* dst = head + (int64_t)row * D * 4;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f32x4 w = {acc[db][i * 4 + 0] * mul, acc[db][i * 4 + 1] * mul, acc[db][i * 4 + 2] * mul,
+                       acc[db][i * 4 + 3] * mul};
+      *reinterpret_cast<f32x4*>(dst + (db * 32 + i * 8 + g * 4) * 4) = w;
+    }
+}
+
+// dQ (float32): one workgroup per 128 query rows, K and V tiles streamed.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kBwdWaves * 64) __attribute__((amdgpu_waves_per_eu(1)))
+void bwd_dq_f32(BwdParams p) {
+  constexpr int NT = kBwdWaves * 64, BC = 32;
+  using KS = RowStage<BC, D * 4, D * 4 + 16, NT>;
+  using VS = RowStage<BC, D * 4, D * 4 + 32, NT>;
+  constexpr int kStage = KS::kBytes + VS::kBytes;
+  __shared__ __attribute__((aligned(16))) char smem[2 * kStage];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, g = lane >> 5;
+  const int blk = xcd_remap(blockIdx.x, p.n_blocks);
+  const int bh = blk / p.n_tiles;
+  const int qt = CAUSAL ? p.n_tiles - 1 - blk % p.n_tiles : blk % p.n_tiles;
+  const int N = p.n;
+  const int64_t head = (int64_t)bh * N * D * 4;
+  const char* K = p.k + head;
+  const char* V = p.v + head;
+
+  const int q_row = qt * kBwdRows + wave * 32 + l32;
+  const int q_ld = min(q_row, N - 1);
+  f32x4 qf[D / 8], dof[D / 8];
+  load_operand_f32<D>(p.q + head, q_ld, g, qf);
+  load_operand_f32<D>(p.dout + head, q_ld, g, dof);
+  const float lse2 = p.lse2[(int64_t)bh * N + q_ld];
+  const float di = p.delta[(int64_t)bh * N + q_ld];
+
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
+  const int n_tiles = (N + BC - 1) / BC;
+  const int n_full = N / BC;
+  const int kt_end = CAUSAL ? min(n_tiles, (qt + 1) * (kBwdRows / BC)) : n_tiles;
+  const int diag = CAUSAL ? (qt * kBwdRows + wave * 32) / BC : n_tiles;
+  const int my_last = min(diag, n_tiles - 1);
+  const int key_lim = CAUSAL ? min(q_row, N - 1) : N - 1;
+
+  KS ks;
+  VS vs;
+  ks.load(K, 0, N, tid);
+  vs.load(V, 0, N, tid);
+  ks.store(smem, tid);
+  vs.store(smem + KS::kBytes, tid);
+  wait_vmem_all();
+  __syncthreads();
+  for (int j = 0; j < kt_end; ++j) {
+    const char* kb = smem + (j & 1) * kStage;
+    const char* vb = kb + KS::kBytes;
+    const bool more = j + 1 < kt_end;
+    if (more) {
+      ks.load(K, (j + 1) * BC, N, tid);
+      vs.load(V, (j + 1) * BC, N, tid);
+    }
+    if (j <= my_last) {
+      // S^T = K Q^T and dP^T = V dO^T (lane = query, registers = keys)
+      f32x16 st = f32x16{}, dpt = f32x16{};
+#pragma unroll
+      for (int i = 0; i < D / 8; ++i) {
+        const f32x4 a = __builtin_bit_cast(f32x4, KS::read16(kb, l32, (i * 8 + g * 4) * 4));
+        const f32x4 b = __builtin_bit_cast(f32x4, VS::read16(vb, l32, (i * 8 + g * 4) * 4));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          st = __builtin_amdgcn_mfma_f32_32x32x2f32(a[e], qf[i][e], st, 0, 0, 0);
+          dpt = __builtin_amdgcn_mfma_f32_32x32x2f32(b[e], dof[i][e], dpt, 0, 0, 0);
+        }
+      }
+      // dS = P (dP - D); hidden keys (past N, or causal after the query) get
+      // an exact zero by selection
+      const int key0 = j * BC;
+      const bool mask = j == n_full || (CAUSAL && j == diag);
+      float ds[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float pr = exp2_fast(fmaf(st[r], p.c, -lse2));
+        ds[r] = pr * (dpt[r] - di);
+        if (mask && key0 + score_key(0, r, g) > key_lim) ds[r] = 0.f;
+      }
+      // dQ^T += K^T dS^T
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(KS::read4(kb, score_key(0, r, g), (db * 32 + l32) * 4),
+                                                         ds[r], acc[db], 0, 0, 0);
+    }
+    if (more) {
+      char* nb = smem + ((j + 1) & 1) * kStage;
+      ks.store(nb, tid);
+      vs.store(nb + KS::kBytes, tid);
+    }
+    __syncthreads();
+  }
+  store_rows_f32<D>(p.dq + head, q_row, N, g, acc, p.scale);
+}
+
+// dK, dV (float32): one workgroup per 128 key rows; Q, dO and the two
+// per-query statistics (LSE*log2(e), D) streamed 32 queries at a time.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kBwdWaves * 64) __attribute__((amdgpu_waves_per_eu(1)))
+void bwd_dkdv_f32(BwdParams p) {
+  constexpr int NT = kBwdWaves * 64, BC = 32;
+  using QS = RowStage<BC, D * 4, D * 4 + 16, NT>;
+  using OS = RowStage<BC, D * 4, D * 4 + 32, NT>;
+  constexpr int kStats = 2 * BC * 4;  // LSE*log2(e) then D, 32 floats each
+  constexpr int kStage = QS::kBytes + OS::kBytes + kStats;
+  __shared__ __attribute__((aligned(16))) char smem[2 * kStage];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, g = lane >> 5;
+  const int blk = xcd_remap(blockIdx.x, p.n_blocks);
+  const int bh = blk / p.n_tiles, kt = blk % p.n_tiles;
+  const int N = p.n;
+  const int64_t head = (int64_t)bh * N * D * 4;
+  const char* Q = p.q + head;
+  const char* dO = p.dout + head;
+  const float* lse_h = p.lse2 + (int64_t)bh * N;
+  const float* del_h = p.delta + (int64_t)bh * N;
+
+  const int key_row = kt * kBwdRows + wave * 32 + l32;
+  const int k_ld = min(key_row, N - 1);
+  f32x4 kf[D / 8], vf[D / 8];
+  load_operand_f32<D>(p.k + head, k_ld, g, kf);
+  load_operand_f32<D>(p.v + head, k_ld, g, vf);
+
+  f32x16 dk[D / 32], dv[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) dk[db] = dv[db] = f32x16{};
+  const int n_tiles = (N + BC - 1) / BC;
+  const int n_full = N / BC;
+  // causal: queries before this workgroup's first key see none of its keys,
+  // and this wave's keys are first seen by its diagonal query tile
+  const int qt_begin = CAUSAL ? min(n_tiles, kt * (kBwdRows / BC)) : 0;
+  const int diag = CAUSAL ? (kt * kBwdRows + wave * 32) / BC : 0;
+
+  // statistics of one query tile: threads 0..31 stage LSE*log2(e), 32..63 D
+  // (queries past N re-read query N-1: in bounds, masked below)
+  float stat = 0.f;
+  auto load_stats = [&](int tile) {
+    if (tid < 2 * BC) stat = (tid < BC ? lse_h : del_h)[min(tile * BC + tid % BC, N - 1)];
+  };
+  auto store_stats = [&](char* st) {
+    if (tid < 2 * BC) reinterpret_cast<float*>(st)[tid] = stat;
+  };
+  QS qs;
+  OS os;
+  if (qt_begin < n_tiles) {
+    qs.load(Q, qt_begin * BC, N, tid);
+    os.load(dO, qt_begin * BC, N, tid);
+    load_stats(qt_begin);
+    qs.store(smem, tid);
+    os.store(smem + QS::kBytes, tid);
+    store_stats(smem + QS::kBytes + OS::kBytes);
+  }
+  wait_vmem_all();
+  __syncthreads();
+  for (int u = qt_begin; u < n_tiles; ++u) {
+    const char* qb = smem + ((u - qt_begin) & 1) * kStage;
+    const char* ob = qb + QS::kBytes;
+    const float* stb = reinterpret_cast<const float*>(ob + OS::kBytes);
+    const bool more = u + 1 < n_tiles;
+    if (more) {
+      qs.load(Q, (u + 1) * BC, N, tid);
+      os.load(dO, (u + 1) * BC, N, tid);
+      load_stats(u + 1);
+    }
+    if (!CAUSAL || u >= diag) {
+      // S = Q K^T and dP = dO V^T (lane = key, registers = queries)
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int i = 0; i < D / 8; ++i) {
+        const f32x4 a = __builtin_bit_cast(f32x4, QS::read16(qb, l32, (i * 8 + g * 4) * 4));
+        const f32x4 b = __builtin_bit_cast(f32x4, OS::read16(ob, l32, (i * 8 + g * 4) * 4));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          s = __builtin_amdgcn_mfma_f32_32x32x2f32(a[e], kf[i][e], s, 0, 0, 0);
+          dp = __builtin_amdgcn_mfma_f32_32x32x2f32(b[e], vf[i][e], dp, 0, 0, 0);
+        }
+      }
+      // P and dS; hidden pairs (query past N, or causal query before the key)
+      // get exact zeros by selection
+      const bool mask = u == n_full || (CAUSAL && u == diag);
+      float pr[16], ds[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int ql = score_key(0, r, g);
+        const float x = exp2_fast(fmaf(s[r], p.c, -stb[ql]));
+        pr[r] = x;
+        ds[r] = x * (dp[r] - stb[BC + ql]);
+        if (mask) {
+          const int qi = u * BC + ql;
+          if (qi >= N || (CAUSAL && qi < key_row)) pr[r] = ds[r] = 0.f;
+        }
+      }
+      // dV^T += dO^T P and dK^T += Q^T dS
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int ql = score_key(0, r, g);
+          dv[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(OS::read4(ob, ql, (db * 32 + l32) * 4), pr[r], dv[db], 0,
+                                                        0, 0);
+          dk[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(QS::read4(qb, ql, (db * 32 + l32) * 4), ds[r], dk[db], 0,
+                                                        0, 0);
+        }
+    }
+    if (more) {
+      char* nb = smem + ((u + 1 - qt_begin) & 1) * kStage;
+      qs.store(nb, tid);
+      os.store(nb + QS::kBytes, tid);
+      store_stats(nb + QS::kBytes + OS::kBytes);
+    }
+    __syncthreads();
+  }
+  store_rows_f32<D>(p.dk + head, key_row, N, g, dk, p.scale);
+  store_rows_f32<D>(p.dv + head, key_row, N, g, dv, 1.f);
+}
+
+// Kernel parameters of one backward pass; *rows = B * H * N.
+BwdParams bwd_params(const BwdArgs& a, int64_t* rows) {
   BwdParams p;
   p.q = static_cast<const char*>(a.q);
   p.k = static_cast<const char*>(a.k);
@@ -550,8 +823,15 @@ hipError_t run_bwd(const BwdArgs& a) {
   p.n_blocks = a.B * a.H * p.n_tiles;
   p.c = a.scale * kLog2e;
   p.scale = a.scale;
-  const int64_t rows = (int64_t)a.B * a.H * a.N;
-  p.lse2 = a.delta + rows;
+  *rows = (int64_t)a.B * a.H * a.N;
+  p.lse2 = a.delta + *rows;
+  return p;
+}
+
+template <class E, int D, bool CAUSAL>
+hipError_t run_bwd(const BwdArgs& a) {
+  int64_t rows;
+  const BwdParams p = bwd_params(a, &rows);
   constexpr int kRowsPerBlock = 4 * (64 / (D / 8));
   hipLaunchKernelGGL((bwd_delta<E, D>), dim3((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock)), dim3(256), 0,
                      a.stream, p, rows);
@@ -560,13 +840,27 @@ hipError_t run_bwd(const BwdArgs& a) {
   return hipGetLastError();
 }
 
+template <int D, bool CAUSAL>
+hipError_t run_bwd_f32(const BwdArgs& a) {
+  int64_t rows;
+  const BwdParams p = bwd_params(a, &rows);
+  constexpr int kRowsPerBlock = 4 * (64 / (D / 4));
+  hipLaunchKernelGGL((bwd_delta_f32<D>), dim3((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock)), dim3(256), 0,
+                     a.stream, p, rows);
+  hipLaunchKernelGGL((bwd_dq_f32<D, CAUSAL>), dim3(p.n_blocks), dim3(kBwdWaves * 64), 0, a.stream, p);
+  hipLaunchKernelGGL((bwd_dkdv_f32<D, CAUSAL>), dim3(p.n_blocks), dim3(kBwdWaves * 64), 0, a.stream, p);
+  return hipGetLastError();
+}
+
 template <bool CAUSAL>
 hipError_t launch_bwd_t(const BwdArgs& a) {
   switch (a.dtype) {
     case kBF16:
       return a.d == 128 ? run_bwd<BF16, 128, CAUSAL>(a) : run_bwd<BF16, 64, CAUSAL>(a);
-    default:
+    case kF16:
       return a.d == 128 ? run_bwd<F16, 128, CAUSAL>(a) : run_bwd<F16, 64, CAUSAL>(a);
+    default:
+      return a.d == 128 ? run_bwd_f32<128, CAUSAL>(a) : run_bwd_f32<64, CAUSAL>(a);
   }
 }
 

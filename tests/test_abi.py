@@ -139,7 +139,7 @@ def bwd(L, ptrs=None, B=1, H=1, N=16, d=64, scale=0.125, dtype=2, causal=False):
 def test_backward_validation(L, causal):
     assert bwd(L, B=-1, causal=causal) == fa.FA_ERR_SHAPE
     assert bwd(L, d=96, causal=causal) == fa.FA_ERR_UNSUPPORTED
-    assert bwd(L, dtype=0, causal=causal) == fa.FA_ERR_UNSUPPORTED  # float32 backward is not provided
+    assert bwd(L, dtype=7, causal=causal) == fa.FA_ERR_UNSUPPORTED
     assert bwd(L, scale=math.nan, causal=causal) == fa.FA_ERR_SCALE
     for i in range(10):  # every pointer is required
         assert bwd(L, {i: None}, causal=causal) == fa.FA_ERR_NULL, i
