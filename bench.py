@@ -16,6 +16,8 @@ drawn with sigma 3). Prints one JSON line:
              rocprofv3 counter summary when it matches the current kernel source
   cpu_baseline  the float64 CPU oracle timed on this host on a bounded sample of
              the same workload (whole query rows, about 15 s of work)
+  also       (default workload only) the kernel time and TFLOP/s of the
+             4096-token case (B=1, H=8, d=128, bf16), the metric's other size
 """
 from __future__ import annotations
 
@@ -61,6 +63,39 @@ def measured_traffic(workload: str, entry: str):
     if not rec or rec.get("source_hash") != kernel_source_hash(entry):
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def time_forward(name: str, steps: int = 20, warmup: int = 5) -> dict:
+    """Kernel time of the fused forward pass on another named workload (HIP
+    events on the launch stream, as for the main line): the metric names both
+    the 4096- and the 32768-token cases."""
+    import numpy as np
+    import torch
+
+    import io_aware_tiled_06_amd as fa
+    from io_aware_tiled_06_amd import traffic
+    from io_aware_tiled_06_amd.workloads import WORKLOADS, make_inputs
+
+    w = WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    tdt = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}[w.dtype]
+    tq, tk, tv = (torch.from_numpy(x).to(tdt).to(dev) for x in make_inputs(w))
+    o = torch.empty_like(tq)
+    for _ in range(warmup):
+        fa.flash_attn_fwd(tq, tk, tv, w.scale, out=o)
+    stream = torch.cuda.current_stream(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize(dev)
+    for a, b in ev:
+        a.record(stream)
+        fa.flash_attn_fwd(tq, tk, tv, w.scale, out=o)
+        b.record(stream)
+    torch.cuda.synchronize(dev)
+    ms = [a.elapsed_time(b) for a, b in ev]
+    tflops = traffic.attention_flops(w.B, w.H, w.N, w.d) / (float(np.mean(ms)) * 1e-3) / 1e12
+    return {"workload": name, "kernel_ms": round(float(np.mean(ms)), 4),
+            "kernel_ms_median": round(float(np.median(ms)), 4), "tflops": round(tflops, 3),
+            "frac_of_peak": round(tflops / PEAK_TFLOPS[w.dtype], 4), "steps": steps}
 
 
 def cpu_baseline(w, q, k, v, target_s: float = 15.0):
@@ -390,6 +425,9 @@ def main() -> int:
     }
     if args.backward:
         line["roofline"]["kernels"] = "bwd_delta + bwd_dq + bwd_dkdv (one backward pass)"
+    if args.entry == "flash" and not (args.causal or args.backward) and w.name == "n32768_d128_bf16":
+        print("[bench] the 4096-token forward (the metric's other case)", file=sys.stderr, flush=True)
+        line["also"] = time_forward("n4096_d128_bf16")
     if not args.no_cpu_baseline and not args.backward:
         print("[bench] cpu baseline (float64 oracle)", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(w, q, k, v)
