@@ -15,6 +15,9 @@ Sources (the pages, by title and section):
     end -- whose output equals standard attention.
   * "What FlashAttention actually buys", "The actual problem": the tiled result
     is exact attention, not an approximation.
+  * "What FlashAttention actually buys", "Why the distinction matters
+    downstream": the backward pass recomputes tiles rather than storing the
+    score matrix; the gradient functions here differentiate the definition.
 
 Readings taken where the pages are silent (each also listed with the design
 notes of this repository):
@@ -229,3 +232,39 @@ def attention_backward_reference(q, k, v, do, scale: float, causal: bool = False
         dq[idx] = s * (ds @ kh)
         dk[idx] = s * (ds.T @ qh)
     return dq, dk, dv
+
+
+def attention_backward_rows(q, k, v, do, scale: float, rows, causal: bool = False):
+    """dQ of attention for the query rows `rows` only, float64.
+
+    Row i of dQ depends on row i alone: with s_j = scale * q_i . k_j over the
+    keys row i sees (all N, or j <= i when causal), p = softmax(s),
+    dp_j = dO_i . v_j and D_i = sum_j p_j dp_j,
+        dQ_i = scale * sum_j p_j (dp_j - D_i) k_j.
+    The same chain rule as attention_backward_reference, evaluated one row at
+    a time, so that it fits very long sequences.
+
+    q, k [..., N, d], v, do [..., N, dv]; rows: query indices. Returns dQ rows
+    [..., len(rows), d], float64.
+    """
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    _check(q, k, v)
+    if do.shape != q.shape[:-1] + (v.shape[-1],):
+        raise ValueError("do must have the shape of the output")
+    nq, nk = q.shape[-2], k.shape[-2]
+    if causal and nq != nk:
+        raise ValueError("causal attention needs as many queries as keys")
+    s = np.float64(scale)
+    rows = [int(i) for i in rows]
+    out = np.empty(q.shape[:-2] + (len(rows), q.shape[-1]), dtype=np.float64)
+    for idx in np.ndindex(*q.shape[:-2]):
+        qh, kh, vh, doh = q[idx], k[idx], v[idx], do[idx]
+        for t, i in enumerate(rows):
+            end = i + 1 if causal else nk
+            sc = s * (kh[:end] @ qh[i])
+            e = np.exp(sc - sc.max())
+            p = e / e.sum()
+            dp = vh[:end] @ doh[i]
+            delta = p @ dp
+            out[idx + (t,)] = s * ((p * (dp - delta)) @ kh[:end])
+    return out

@@ -147,3 +147,59 @@ from pins import BWD_PINS  # noqa: E402
 @pytest.mark.parametrize("pin", BWD_PINS, ids=lambda p: p.__name__)
 def test_backward_reference_meets_pin(pin):
     pin(lambda q, k, v, do, s, causal: attention_backward_reference(q, k, v, do, s, causal=causal))
+
+
+# -- row-wise dQ (long sequences) -------------------------------------------------
+
+from oracle import attention_backward_rows  # noqa: E402
+
+
+def test_backward_rows_against_library_autograd():
+    """torch's float64 autograd through its own CPU attention, sampled rows."""
+    import torch
+    import torch.nn.functional as F
+
+    rng = np.random.default_rng(410)
+    for causal in (False, True):
+        q, k, v, do = (rng.standard_normal((2, 3, 57, 16)) for _ in range(4))
+        scale = 0.3
+        rows = [0, 1, 20, 55, 56]
+        got = attention_backward_rows(q, k, v, do, scale, rows, causal=causal)
+        tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+        o = F.scaled_dot_product_attention(tq, tk, tv, scale=scale, is_causal=causal)
+        o.backward(torch.from_numpy(do))
+        assert np.max(np.abs(got - tq.grad.numpy()[:, :, rows])) <= 1e-12, causal
+
+
+def test_backward_rows_finite_differences():
+    """dQ entries against a central difference of L = sum(O * dO) with the
+    (separately pinned) forward oracle."""
+    from oracle import attention_reference
+
+    rng = np.random.default_rng(411)
+    for causal in (False, True):
+        q, k, v, do = (rng.standard_normal((1, 6, 4)) for _ in range(4))
+        got = attention_backward_rows(q, k, v, do, 0.9, range(6), causal=causal)
+        h = 1e-5
+        for idx in np.ndindex(*q.shape):
+            qp, qm = q.copy(), q.copy()
+            qp[idx] += h
+            qm[idx] -= h
+            lp = np.sum(attention_reference(qp, k, v, 0.9, causal=causal)[0] * do)
+            lm = np.sum(attention_reference(qm, k, v, 0.9, causal=causal)[0] * do)
+            fd = (lp - lm) / (2 * h)
+            assert abs(got[idx] - fd) <= 2e-8 * max(1.0, abs(fd)), (causal, idx)
+
+
+def test_backward_rows_closed_forms():
+    """One key, or scale 0 (uniform weights): dQ = 0 exactly in exact
+    arithmetic; and the rows equal the full-matrix gradient's rows."""
+    rng = np.random.default_rng(412)
+    q, k, v, do = (rng.standard_normal((2, 1, 5)) for _ in range(4))
+    assert np.max(np.abs(attention_backward_rows(q, k, v, do, 0.7, [0]))) <= 1e-15
+    q, k, v, do = (rng.standard_normal((1, 30, 5)) for _ in range(4))
+    for causal in (False, True):
+        assert np.max(np.abs(attention_backward_rows(q, k, v, do, 0.0, [0, 7, 29], causal=causal))) <= 1e-15
+        full = attention_backward_reference(q, k, v, do, 0.45, causal=causal)[0]
+        got = attention_backward_rows(q, k, v, do, 0.45, [3, 0, 29], causal=causal)
+        assert np.max(np.abs(got - full[:, [3, 0, 29]])) <= 1e-13
