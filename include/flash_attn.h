@@ -1,8 +1,10 @@
 /*
- * flash_attn.h -- C interface of libflashattn.so: exact non-causal scaled
- * dot-product attention on an AMD Instinct MI355X (gfx950).
+ * flash_attn.h -- C interface of libflashattn.so: exact scaled dot-product
+ * attention on an AMD Instinct MI355X (gfx950) -- the fused forward pass
+ * (non-causal and causal), its gradients, and a three-pass comparator.
  *
- * The operation (all entry points):
+ * The operation (forward entry points; the causal form restricts row i to
+ * keys 0..i, see flash_attn_fwd_causal):
  *   for every batch b and head h, with S = scale * Q K^T over the N tokens,
  *     O   = softmax_rows(S) V
  *     LSE = ln sum_j exp(S_ij)                 (natural log, one per query row)
