@@ -29,6 +29,7 @@
 // no work of a step waits on a product issued in the same step. bwd_dq forms
 // tile t's S and dP first and covers their latency with tile t-1's dQ
 // product (fewer live registers: two waves per SIMD also for causal).
+#include <atomic>
 #include "fa_device.h"
 #include "fa_launch.h"
 
@@ -56,6 +57,10 @@ struct BwdParams {
 };
 
 constexpr int kBwdWaves = 4;
+constexpr int kDkdvWideWaves = 8;  // bwd_dkdv8
+#ifndef FA_BWD_WIDE
+#define FA_BWD_WIDE 1
+#endif
 constexpr int kBwdRows = kBwdWaves * 32;  // rows (queries or keys) per workgroup
 
 // ---------------------------------------------------------------------------
@@ -533,6 +538,209 @@ void bwd_dkdv(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// dK, dV at d = 128 on large grids, non-causal: 8 waves, 256 keys per
+// workgroup, two waves per SIMD. (The causal mask's extra state does not
+// fit in the 256 registers two waves per SIMD allow; causal attention keeps
+// bwd_dkdv.) Keeping V in registers as well as K and both accumulators
+// would need about 400 registers (one wave per SIMD, bwd_dkdv); here each
+// wave's 32 V rows are staged once into LDS and read from there as the B
+// operand of dP. They are kept unswizzled at a padded pitch (rows 4 banks
+// apart: 16-byte row reads are conflict free), so a read's chunk offset is
+// a constant in the instruction and one register addresses them all.
+//
+// Half-pipelined like bwd_dq: step u forms S and dP of query tile u, then
+// adds tile u-1's dV and dK products (independent of them), then forms P and
+// dS of tile u. Tile u is read as rows in step u and transposed in step u+1;
+// step u copies tile u+2 into tile u-2's slot of a 4-slot ring (last read in
+// step u-1); at its end tile u+1 must have landed (only step u's copies may
+// still be in flight).
+// ---------------------------------------------------------------------------
+template <class E, int D>
+__global__ __launch_bounds__(kDkdvWideWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void bwd_dkdv8(BwdParams p) {
+  static_assert(D == 128, "8-wave copies need 1 KB per wave per tile");
+  constexpr int NW = kDkdvWideWaves, NBUF = 4, KK = D / 16, DB = D / 32;
+  constexpr int KR = NW * 32;  // keys per workgroup
+  constexpr int kTile = 32 * D * 2;
+  constexpr int PER = kTile / 1024 / NW;
+  constexpr int kStats = 256;  // 32 LSE*log2(e) floats then 32 D floats
+  constexpr int kSlot = 2 * kTile + kStats;
+  constexpr int RB = D * 2, kVPitch = RB + 16;  // V row bytes, padded pitch
+  __shared__ __attribute__((aligned(1024))) char smem[NBUF * kSlot + NW * 32 * kVPitch];
+  auto qbuf = [&](int b) { return smem + b * kSlot; };
+  auto dobuf = [&](int b) { return smem + b * kSlot + kTile; };
+  auto stbuf = [&](int b) { return smem + b * kSlot + 2 * kTile; };
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, g = lane >> 5;
+  char* const vrows = smem + NBUF * kSlot + wave * 32 * kVPitch;  // this wave's 32 V rows
+  const int blk = xcd_remap(blockIdx.x, p.n_blocks);
+  const int bh = blk / p.n_tiles, kt = blk % p.n_tiles;
+  const int N = p.n;
+  const int64_t head = (int64_t)bh * N * D * 2;
+  const float* lse_h = p.lse2 + (int64_t)bh * N;
+  const float* del_h = p.delta + (int64_t)bh * N;
+
+  TileCopy<D, PER> cp;
+  cp.init(wave, lane);
+  DualOffsets<D> off;
+  off.init(lane);
+  auto copy_stats = [&](int tile, char* dst) {
+    if (wave < 2 && lane < 32) {
+      const float* src = wave == 0 ? lse_h : del_h;
+      const int row0 = tile * 32;
+      const i32x4 rs = buffer_rsrc(src + row0, 128);
+      load_lds4(rs, lds_addr(dst) + wave * 128, min(lane, N - 1 - row0) * 4);
+    }
+  };
+
+  const int key_row = kt * KR + wave * 32 + l32;
+  const int k_ld = min(key_row, N - 1);
+  u32x4 kf[KK];
+  load_operand<D>(p.k + head, k_ld, g, kf);
+  {
+    // this wave's 32 V rows, 16 bytes per lane and load (rows past N re-read
+    // row N-1; a wave whose keys all lie past N stages the last real tile,
+    // and its results are never stored)
+    const int vt = min(kt * (KR / 32) + wave, (N - 1) / 32);
+#pragma unroll
+    for (int i = 0; i < 32 * RB / 16 / 64; ++i) {
+      const int item = i * 64 + lane, r = item / (RB / 16), c = item % (RB / 16);
+      const int key = min(vt * 32 + r, N - 1);
+      *reinterpret_cast<u32x4*>(vrows + r * kVPitch + c * 16) = ld_global16(p.v + head + (int64_t)key * RB + c * 16);
+    }
+  }
+  const uint32_t v_lane = l32 * kVPitch + g * 16;  // row l32, chunk 2 kk + g at + 32 kk
+  __builtin_amdgcn_sched_barrier(0);
+
+  const int cnt = (N + 31) / 32;  // query tiles
+  const int n_full = N / 32;
+  auto issue = [&](int u, int b) {
+    cp.copy(p.q + head, u, N, qbuf(b), wave);
+    cp.copy(p.dout + head, u, N, dobuf(b), wave);
+    copy_stats(u, stbuf(b));
+  };
+  for (int u = 0; u < 2; ++u)
+    if (u < cnt) issue(u, u);
+
+  f32x16 dk[DB], dv[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) dk[db] = dv[db] = f32x16{};
+
+  // S = Q K^T and dP = dO V^T of one tile (lane = key, registers = queries).
+  auto scores = [&](int b, f32x16& s, f32x16& dp) {
+    s = f32x16{};
+    dp = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      s = Mfma<E>::run(off.read_row(qbuf(b), kk), kf[kk], s);
+      dp = Mfma<E>::run(off.read_row(dobuf(b), kk), *reinterpret_cast<const u32x4*>(vrows + v_lane + kk * 32), dp);
+    }
+  };
+  // P and dS of one tile (as bwd_dkdv).
+  auto grad_scores = [&](int b, int u, const f32x16& s, const f32x16& dp, u32x4(&pf)[2], u32x4(&dsf)[2],
+                         bool mask) {
+    const float* st = reinterpret_cast<const float*>(stbuf(b));
+    float pr[16], ds[16];
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(st + rr * 8 + g * 4);
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(st + 32 + rr * 8 + g * 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = rr * 4 + e;
+        const float x = exp2_fast(fmaf(s[r], p.c, -l4[e]));
+        pr[r] = x;
+        ds[r] = x * (dp[r] - d4[e]);
+        if (mask && u * 32 + score_key(0, r, g) >= N) pr[r] = ds[r] = 0.f;
+      }
+    }
+    pack_operand<E>(pr, pf);
+    pack_operand<E>(ds, dsf);
+  };
+  // dV^T += dO^T P and dK^T += Q^T dS of one tile.
+  auto accumulate = [&](int b, const u32x4(&pf)[2], const u32x4(&dsf)[2]) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        dv[db] = Mfma<E>::run(off.read_t(dobuf(b), db, h), pf[h], dv[db]);
+        dk[db] = Mfma<E>::run(off.read_t(qbuf(b), db, h), dsf[h], dk[db]);
+      }
+  };
+
+  // K, the V rows and the first two tiles have landed (a wait the compiler
+  // sees: it then puts none of its own in the loop).
+  wait_vmem_all();
+  __syncthreads();
+  u32x4 pb[2][2], db_[2][2];  // P and dS of the current and the previous tile
+
+  // STEADY: the slot is known at compile time, the copy exists and is whole
+  // and no tile needs a mask; otherwise decided at run time (workgroup-wide
+  // decisions and this wave's own kept apart, so every wave passes the same
+  // barriers).
+  auto step = [&](int u, const u32x4(&p_prev)[2], const u32x4(&ds_prev)[2], u32x4(&p_cur)[2],
+                  u32x4(&ds_cur)[2], auto slot_tag, auto steady_tag) {
+    constexpr bool STEADY = decltype(steady_tag)::value;
+    const int b = STEADY ? decltype(slot_tag)::value : u % NBUF;
+    const bool copy = STEADY || u + 2 < cnt;
+    if (copy) issue(u + 2, (b + 2) % NBUF);
+    f32x16 s, dp;
+    scores(b, s, dp);
+    if (STEADY || u >= 1) accumulate((b + NBUF - 1) % NBUF, p_prev, ds_prev);
+    // tile u's P and dS wait for its score products anyway; keeping them
+    // after tile u-1's products lets both pairs share registers
+    __builtin_amdgcn_sched_barrier(0);
+    grad_scores(b, u, s, dp, p_cur, ds_cur, !STEADY && u == n_full);
+    if (copy) {
+      if (wave < 2)
+        vm_wait<2 * PER + 1>();
+      else
+        vm_wait<2 * PER>();
+    } else {
+      vm_wait<0>();
+    }
+    __syncthreads();
+  };
+  using T = std::true_type;
+  using F = std::false_type;
+  auto rotate = [&]() {
+    pb[1][0] = pb[0][0];
+    pb[1][1] = pb[0][1];
+    db_[1][0] = db_[0][0];
+    db_[1][1] = db_[0][1];
+  };
+  // step 0 has no previous tile: run it at run time
+  step(0, pb[1], db_[1], pb[0], db_[0], std::integral_constant<int, 0>{}, F{});
+  rotate();
+  int u = 1;
+  // steady groups of four from u = 1: copies up to tile u + 5 exist and are
+  // whole, and no tile of the group is the ragged last one
+#define FA_BWD8_STEP(I)                                                                          \
+  step(u + (I), pb[((I) + 1) % 2], db_[((I) + 1) % 2], pb[(I) % 2], db_[(I) % 2],                \
+       std::integral_constant<int, ((I) + 1) % NBUF>{}, T{})
+  for (; u + 5 < cnt && u + 5 < n_full; u += 4) {
+    FA_BWD8_STEP(0);
+    FA_BWD8_STEP(1);
+    FA_BWD8_STEP(2);
+    FA_BWD8_STEP(3);
+  }
+#undef FA_BWD8_STEP
+  for (; u < cnt; ++u) {
+    step(u, pb[1], db_[1], pb[0], db_[0], std::integral_constant<int, 0>{}, F{});
+    rotate();
+  }
+  accumulate((cnt - 1) % NBUF, pb[1], db_[1]);
+  // an opaque copy of the row index: the compiler would otherwise form the
+  // 64-bit store addresses before the loop and keep them live through it
+  int kr = key_row;
+  asm volatile("" : "+v"(kr));
+  store_rows_t<E, D>(p.dk + head, kr, N, g, dk, p.scale);
+  store_rows_t<E, D>(p.dv + head, kr, N, g, dv, 1.f);
+}
+
+// ---------------------------------------------------------------------------
 // float32 inputs: the same three steps with every value in float32, products
 // on the float32 matrix cores (32x32x2: lane l supplies A[l%32][l/32] and
 // B[l/32][l%32], one element each). Tiles are staged through registers into
@@ -828,6 +1036,20 @@ BwdParams bwd_params(const BwdArgs& a, int64_t* rows) {
   return p;
 }
 
+// Compute units of the current device (cached per device; concurrent first
+// calls store the same value).
+int bwd_device_cus() {
+  static std::atomic<int> cus[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cus[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 template <class E, int D, bool CAUSAL>
 hipError_t run_bwd(const BwdArgs& a) {
   int64_t rows;
@@ -836,6 +1058,18 @@ hipError_t run_bwd(const BwdArgs& a) {
   hipLaunchKernelGGL((bwd_delta<E, D>), dim3((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock)), dim3(256), 0,
                      a.stream, p, rows);
   hipLaunchKernelGGL((bwd_dq<E, D, CAUSAL>), dim3(p.n_blocks), dim3(kBwdWaves * 64), 0, a.stream, p);
+  if constexpr (D == 128 && !CAUSAL) {
+    // 256-key workgroups, two waves per SIMD, when the grid still has at
+    // least two of them per CU
+    constexpr int kKeys = kDkdvWideWaves * 32;
+    BwdParams w = p;
+    w.n_tiles = (a.N + kKeys - 1) / kKeys;
+    w.n_blocks = a.B * a.H * w.n_tiles;
+    if (FA_BWD_WIDE && w.n_blocks >= 2 * bwd_device_cus()) {
+      hipLaunchKernelGGL((bwd_dkdv8<E, D>), dim3(w.n_blocks), dim3(kDkdvWideWaves * 64), 0, a.stream, w);
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL((bwd_dkdv<E, D, CAUSAL>), dim3(p.n_blocks), dim3(kBwdWaves * 64), 0, a.stream, p);
   return hipGetLastError();
 }

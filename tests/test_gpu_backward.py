@@ -197,3 +197,17 @@ def test_backward_long_context(causal):
     rel_dv = float(np.linalg.norm(lhs - rhs) / np.linalg.norm(rhs))
     print(f"[bwd] n32768 causal={causal} sum_j dV_j vs sum_i dO_i: rel={rel_dv:.2e}", flush=True)
     assert rel_dv <= 2.5 * UNIT[w.dtype]
+
+
+@pytest.mark.parametrize("B,H,dtype", [(4, 32, "bf16"), (2, 64, "fp16")])
+def test_backward_wide_key_workgroups(B, H, dtype):
+    """Grids with at least two 256-key workgroups per CU of a 256-CU MI355X
+    (B * H * ceil(N / 256) = 512), which take the 8-wave dK/dV kernel at
+    d = 128 (non-causal), with a ragged length (1000 = 31 * 32 + 8); all three
+    gradients against the oracle."""
+    w = Workload("bwdw", B, H, 1000, 128, dtype, 71, 2.0)
+    q, k, v = make_inputs(w)
+    do = upstream(w, 72)
+    got = run_backward(w, q, k, v, do, w.scale, False)
+    ref = attention_backward_reference(q, k, v, do, w.scale)
+    check(got, ref, f"wide B{B} H{H} N1000 {dtype}", dtype)
