@@ -58,6 +58,10 @@ struct BwdParams {
 
 constexpr int kBwdWaves = 4;
 constexpr int kDkdvWideWaves = 8;  // bwd_dkdv8
+constexpr int kDqWideWaves = 8;    // bwd_dq on 256-row query tiles
+#ifndef FA_BWD_DQ_WIDE
+#define FA_BWD_DQ_WIDE 1
+#endif
 #ifndef FA_BWD_WIDE
 #define FA_BWD_WIDE 1
 #endif
@@ -202,10 +206,11 @@ __device__ __forceinline__ void store_rows_t(char* head, int row, int n, int g, 
 // its end K_{t+1} and V_{t+1} must have landed: this step's copies may still
 // be in flight.
 // ---------------------------------------------------------------------------
-template <class E, int D, bool CAUSAL>
-__global__ __launch_bounds__(kBwdWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
+template <class E, int D, bool CAUSAL, int NW = kBwdWaves>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void bwd_dq(BwdParams p) {
-  constexpr int NW = kBwdWaves, NBUF = 4, KK = D / 16, DB = D / 32;
+  constexpr int NBUF = 4, KK = D / 16, DB = D / 32;
+  constexpr int BR = NW * 32;  // query rows per workgroup
   constexpr int kTile = 32 * D * 2;
   constexpr int PER = kTile / 1024 / NW;
   __shared__ __attribute__((aligned(1024))) char smem[2 * NBUF * kTile];  // K ring, V ring
@@ -226,7 +231,7 @@ void bwd_dq(BwdParams p) {
   DualOffsets<D> off;
   off.init(lane);
 
-  const int q_row = qt * kBwdRows + wave * 32 + l32;
+  const int q_row = qt * BR + wave * 32 + l32;
   const int q_ld = min(q_row, N - 1);
   u32x4 qf[KK], dof[KK];
   load_operand<D>(p.q + head, q_ld, g, qf);
@@ -237,8 +242,8 @@ void bwd_dq(BwdParams p) {
 
   const int n_tiles = (N + 31) / 32;
   const int n_full = N / 32;
-  const int kt_end = CAUSAL ? min(n_tiles, (qt + 1) * (kBwdRows / 32)) : n_tiles;
-  const int diag = CAUSAL ? (qt * kBwdRows + wave * 32) / 32 : n_tiles;
+  const int kt_end = CAUSAL ? min(n_tiles, (qt + 1) * (BR / 32)) : n_tiles;
+  const int diag = CAUSAL ? (qt * BR + wave * 32) / 32 : n_tiles;
   const int my_last = min(diag, n_tiles - 1);
   const int key_lim = CAUSAL ? min(q_row, N - 1) : N - 1;
   // Ring start, virtual steps -3..-1 (K first in each): V0; K0, V1; K1, V2.
@@ -309,7 +314,7 @@ void bwd_dq(BwdParams p) {
   int t = 0;
   // steady groups of four from t = 0 (mod 4): every copy exists and is whole,
   // every tile lies below every wave's diagonal and needs no mask
-  const int steady_end = CAUSAL ? min(n_full, qt * (kBwdRows / 32)) : n_full;
+  const int steady_end = CAUSAL ? min(n_full, qt * (BR / 32)) : n_full;
 #define FA_BWD_STEP(I) step(t + (I), db_[((I) + 1) % 2], db_[(I) % 2], std::integral_constant<int, (I) % NBUF>{}, T{})
   // step 0 has no previous tile: run it at run time
   step(0, db_[1], db_[0], std::integral_constant<int, 0>{}, F{});
@@ -1057,7 +1062,21 @@ hipError_t run_bwd(const BwdArgs& a) {
   constexpr int kRowsPerBlock = 4 * (64 / (D / 8));
   hipLaunchKernelGGL((bwd_delta<E, D>), dim3((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock)), dim3(256), 0,
                      a.stream, p, rows);
-  hipLaunchKernelGGL((bwd_dq<E, D, CAUSAL>), dim3(p.n_blocks), dim3(kBwdWaves * 64), 0, a.stream, p);
+  bool dq_done = false;
+  if constexpr (D == 128) {
+    // 256-row query tiles (8 waves) when the grid still has at least two of
+    // them per CU: each K/V tile reaches LDS once for twice the rows
+    constexpr int kRows = kDqWideWaves * 32;
+    BwdParams w = p;
+    w.n_tiles = (a.N + kRows - 1) / kRows;
+    w.n_blocks = a.B * a.H * w.n_tiles;
+    if (FA_BWD_DQ_WIDE && w.n_blocks >= 2 * bwd_device_cus()) {
+      hipLaunchKernelGGL((bwd_dq<E, D, CAUSAL, kDqWideWaves>), dim3(w.n_blocks), dim3(kDqWideWaves * 64), 0,
+                         a.stream, w);
+      dq_done = true;
+    }
+  }
+  if (!dq_done) hipLaunchKernelGGL((bwd_dq<E, D, CAUSAL>), dim3(p.n_blocks), dim3(kBwdWaves * 64), 0, a.stream, p);
   if constexpr (D == 128 && !CAUSAL) {
     // 256-key workgroups, two waves per SIMD, when the grid still has at
     // least two of them per CU
