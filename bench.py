@@ -65,6 +65,90 @@ def measured_traffic(workload: str, entry: str):
     return rec.get("hbm_bytes_per_launch")
 
 
+class ClockSampler:
+    """Samples the GPU's shader clock and board power while the timed loop runs.
+
+    Reads the driver's sysfs files of the one GPU card present: the current
+    shader-clock level (``pp_dpm_sclk``, the line marked ``*``) and the board
+    power (hwmon ``power1_input``, microwatts) every ``period`` seconds from a
+    host thread. The matrix-core peak assumes the full 2.4 GHz clock; under
+    sustained dense work the card may run slower. The driver's clock figure is
+    the firmware's smoothed value, not a cycle count: it shows the trend, while
+    the exact cycles of a launch come from the GRBM_COUNT counter under
+    rocprofv3. Gives None where the files are absent or more than one card is
+    present (the card could not be told apart).
+    """
+
+    def __init__(self, period: float = 0.005, root: str = "/sys/class/drm"):
+        import glob
+        import threading
+
+        self.period = period
+        self.sclk, self.power = [], []
+        cards = [c for c in sorted(glob.glob(os.path.join(root, "card*", "device")))
+                 if os.path.exists(os.path.join(c, "pp_dpm_sclk"))]
+        self.card = cards[0] if len(cards) == 1 else None
+        self.power_file = None
+        self.cap_w = None
+        if self.card:
+            hw = sorted(glob.glob(os.path.join(self.card, "hwmon", "hwmon*")))
+            if hw and os.path.exists(os.path.join(hw[0], "power1_input")):
+                self.power_file = os.path.join(hw[0], "power1_input")
+                try:
+                    with open(os.path.join(hw[0], "power1_cap")) as f:
+                        self.cap_w = int(f.read()) / 1e6
+                except (OSError, ValueError):
+                    pass
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    def _sample(self) -> None:
+        import re
+
+        try:
+            with open(os.path.join(self.card, "pp_dpm_sclk")) as f:
+                for ln in f:
+                    m = re.search(r"(\d+)\s*[Mm]hz\s*\*", ln)
+                    if m:
+                        self.sclk.append(int(m.group(1)))
+                        break
+            if self.power_file:
+                with open(self.power_file) as f:
+                    self.power.append(int(f.read()) / 1e6)
+        except (OSError, ValueError):
+            pass
+
+    def _run(self) -> None:
+        while not self._stop.is_set():
+            self._sample()
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        if self.card:
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        if self.card:
+            self._stop.set()
+            self._thread.join()
+        return False
+
+    def summary(self):
+        if not self.sclk:
+            return None
+        import statistics
+
+        out = {"sclk_mhz_median": statistics.median(self.sclk), "sclk_mhz_min": min(self.sclk),
+               "sclk_mhz_max": max(self.sclk), "samples": len(self.sclk),
+               "source": "sysfs pp_dpm_sclk (marked level) and hwmon power1_input, sampled during the timed loop"}
+        if self.power:
+            out["power_w_median"] = round(statistics.median(self.power), 1)
+        if self.cap_w:
+            out["power_cap_w"] = self.cap_w
+        return out
+
+
 def time_forward(name: str, steps: int = 20, warmup: int = 5) -> dict:
     """Kernel time of the fused forward pass on another named workload (HIP
     events on the launch stream, as for the main line): the metric names both
@@ -368,13 +452,14 @@ def main() -> int:
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
     torch.cuda.synchronize(dev)
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        ev[i][0].record(stream)
-        step()
-        ev[i][1].record(stream)
-    torch.cuda.synchronize(dev)
-    wall = time.perf_counter() - t0
+    with ClockSampler() as clk:
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            ev[i][0].record(stream)
+            step()
+            ev[i][1].record(stream)
+        torch.cuda.synchronize(dev)
+        wall = time.perf_counter() - t0
     ev_ms = [a.elapsed_time(b) for a, b in ev]
 
     flops = traffic.attention_flops(w.B, w.H, w.N, w.d)
@@ -423,6 +508,11 @@ def main() -> int:
         "device_cus": torch.cuda.get_device_properties(dev).multi_processor_count,
         "peak_formula": "256 CUs x 2.4 GHz x 4096 FLOP/clk/CU (dense bf16/fp16 matrix cores); fp32: 157.3 TFLOP/s",
     }
+    clock = clk.summary()
+    if clock:
+        # driver telemetry only: the firmware's clock figure is a smoothed value;
+        # the exact cycles of a launch come from the GRBM_COUNT counter
+        line["clock"] = clock
     if args.backward:
         line["roofline"]["kernels"] = "bwd_delta + bwd_dq + bwd_dkdv (one backward pass)"
     if args.entry == "flash" and not (args.causal or args.backward) and w.name == "n32768_d128_bf16":
