@@ -44,10 +44,16 @@ KERNEL_SOURCES = {"flash": ("flash_fwd.hip", "fa_device.h"), "naive": ("naive.hi
 
 
 def kernel_source_hash(entry: str = "flash") -> str:
+    """Hash of the sources a timed kernel is built from, and of any
+    per-source code-generation flags of the build (they change the binary)."""
+    from io_aware_tiled_06_amd.build import SOURCE_FLAGS
+
     h = hashlib.sha256()
     for name in sorted(KERNEL_SOURCES[entry]):
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
+        if SOURCE_FLAGS.get(name):
+            h.update(b"\0flags\0" + " ".join(SOURCE_FLAGS[name]).encode())
     return h.hexdigest()[:16]
 
 
@@ -63,6 +69,73 @@ def measured_traffic(workload: str, entry: str):
     if not rec or rec.get("source_hash") != kernel_source_hash(entry):
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def _counter_rows(path: str, counter: str):
+    """(dispatch id, kernel name, grid size, value) of one counter in a
+    rocprofv3 --pmc counter_collection.csv, in dispatch order."""
+    import csv
+
+    with open(path, newline="") as f:
+        rows = [(int(r["Dispatch_Id"]), r["Kernel_Name"], r["Grid_Size"], float(r["Counter_Value"]))
+                for r in csv.DictReader(f) if r["Counter_Name"] == counter]
+    return sorted(rows)
+
+
+def record_traffic(fetch_csv: str, write_csv: str, copy_fetch_csv: str, copy_write_csv: str,
+                   workload: str = "n32768_d128_bf16", entry: str = "flash",
+                   copy_bytes: int = 1 << 30) -> dict:
+    """Write the HBM-traffic record of `workload` into profiles/traffic.json.
+
+    Inputs: the counter files of four rocprofv3 --pmc runs: FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch) of `bench.py --steps 2 --warmup 1
+    --no-cpu-baseline`, and the same two counters for `bench.py
+    --copy-calibration 1073741824`. The kernel is the first one dispatched
+    (the workload's launch); its first dispatch (warm-up) is left out and the
+    rest averaged. Each counter is scaled so that the copy reads and writes
+    exactly `copy_bytes`. The record carries the current kernel source hash,
+    so bench.py uses it only for the binary it was taken on.
+    """
+    from io_aware_tiled_06_amd import traffic
+    from io_aware_tiled_06_amd.workloads import WORKLOADS
+
+    def kernel_mean(path, counter):
+        rows = _counter_rows(path, counter)
+        name, grid = rows[0][1], rows[0][2]
+        vals = [v for _, n, g, v in rows if n == name and g == grid][1:]
+        if not vals:
+            raise ValueError(f"{path}: no timed dispatch of {name}")
+        return name, sum(vals) / len(vals)
+
+    def copy_mean(path, counter):
+        vals = [v for _, n, _, v in _counter_rows(path, counter) if "copyBuffer" in n]
+        if not vals:
+            raise ValueError(f"{path}: no copy dispatch")
+        return sum(vals) / len(vals)
+
+    name, fetch = kernel_mean(fetch_csv, "FETCH_SIZE")
+    _, write = kernel_mean(write_csv, "WRITE_SIZE")
+    cf, cw = copy_mean(copy_fetch_csv, "FETCH_SIZE"), copy_mean(copy_write_csv, "WRITE_SIZE")
+    fs, ws = copy_bytes / (cf * 1024), copy_bytes / (cw * 1024)
+    w = WORKLOADS[workload]
+    rd, wr = round(fetch * 1024 * fs), round(write * 1024 * ws)
+    short = name.replace("void fa::(anonymous namespace)::", "").split("(")[0].replace("fa::", "").replace(" ", "")
+    try:
+        with open(TRAFFIC_FILE) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        data = {}
+    data[f"{entry}:{workload}"] = {
+        "source_hash": kernel_source_hash(entry), "kernel": short,
+        "fetch_kib_per_dispatch": fetch, "write_kib_per_dispatch": write,
+        "fetch_scale": round(fs, 6), "write_scale": round(ws, 6),
+        "hbm_read_bytes_per_launch": rd, "hbm_write_bytes_per_launch": wr, "hbm_bytes_per_launch": rd + wr,
+        "compulsory_bytes": traffic.compulsory_bytes(w.B, w.H, w.N, w.d, w.elem_bytes),
+    }
+    data["_calibration"] = {"copy_bytes": copy_bytes, "copy_fetch_kib": cf, "copy_write_kib": cw}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(data, f, indent=1)
+    return data[f"{entry}:{workload}"]
 
 
 class ClockSampler:
@@ -389,9 +462,14 @@ def main() -> int:
                     help="only run a plain device copy of BYTES (counter calibration) and exit")
     ap.add_argument("--traffic-sweep", choices=["flash", "naive"], default=None,
                     help="only run the N sweep used for the traffic-versus-N counters and exit")
+    ap.add_argument("--record-traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="write profiles/traffic.json from four rocprofv3 --pmc counter files and exit (no GPU)")
     ap.add_argument("--crossover-sweep", action="store_true",
                     help="only run the fused-versus-three-pass sweep at fixed work (time and memory) and exit")
     args = ap.parse_args()
+    if args.record_traffic:
+        print(json.dumps(record_traffic(*args.record_traffic, workload=args.workload)), flush=True)
+        return 0
     if args.copy_calibration:
         copy_calibration(args.copy_calibration, 3)
         return 0

@@ -45,3 +45,41 @@ def test_sampler_absent_or_ambiguous(tmp_path):
     with bench.ClockSampler(root=str(tmp_path)) as c:
         pass
     assert c.summary() is None
+
+
+# -- the HBM-traffic record written from rocprofv3 counter files ---------------
+
+HEADER = ('"Correlation_Id","Dispatch_Id","Agent_Id","Queue_Id","Process_Id","Thread_Id","Grid_Size",'
+          '"Kernel_Id","Kernel_Name","Workgroup_Size","LDS_Block_Size","Scratch_Size","VGPR_Count",'
+          '"Accum_VGPR_Count","SGPR_Count","Counter_Name","Counter_Value","Start_Timestamp","End_Timestamp"\n')
+KERN = "void fa::(anonymous namespace)::flash_fwd_half<fa::BF16, 128, 8, 1, false, false>(fa::FwdParams)"
+OTHER = "void fa::(anonymous namespace)::flash_fwd_half<fa::BF16, 128, 4, 2, false, false>(fa::FwdParams)"
+COPY = "__amd_rocclr_copyBuffer"
+
+
+def _csv(path, counter, rows):
+    with open(path, "w") as f:
+        f.write(HEADER)
+        for i, (name, grid, val) in enumerate(rows, 1):
+            f.write(f'{i},{i},"Agent 1",1,1,1,{grid},1,"{name}",512,0,0,0,0,0,"{counter}",{val},0,1\n')
+    return str(path)
+
+
+def test_record_traffic(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "traffic.json"))
+    # warm-up dispatch (left out), two timed ones, then another kernel (ignored)
+    f = _csv(tmp_path / "f.csv", "FETCH_SIZE", [(KERN, 1048576, 999.0), (KERN, 1048576, 100.0),
+                                                 (KERN, 1048576, 300.0), (OTHER, 131072, 7.0)])
+    w = _csv(tmp_path / "w.csv", "WRITE_SIZE", [(KERN, 1048576, 5.0), (KERN, 1048576, 50.0),
+                                                 (KERN, 1048576, 70.0), (OTHER, 131072, 7.0)])
+    cf = _csv(tmp_path / "cf.csv", "FETCH_SIZE", [("elementwise", 1, 1.0), (COPY, 1, 512.0), (COPY, 1, 512.0)])
+    cw = _csv(tmp_path / "cw.csv", "WRITE_SIZE", [(COPY, 1, 1024.0), (COPY, 1, 1024.0)])
+    rec = bench.record_traffic(f, w, cf, cw, copy_bytes=1 << 20)
+    # copy of 1 MiB read as 512 KiB -> fetch scale 2; written as 1024 KiB -> scale 1
+    assert rec["fetch_scale"] == 2.0 and rec["write_scale"] == 1.0
+    assert rec["fetch_kib_per_dispatch"] == 200.0 and rec["write_kib_per_dispatch"] == 60.0
+    assert rec["hbm_read_bytes_per_launch"] == 200 * 1024 * 2
+    assert rec["hbm_write_bytes_per_launch"] == 60 * 1024
+    assert rec["kernel"] == "flash_fwd_half<BF16,128,8,1,false,false>"
+    assert rec["source_hash"] == bench.kernel_source_hash("flash")
+    assert bench.measured_traffic("n32768_d128_bf16", "flash") == rec["hbm_bytes_per_launch"]
