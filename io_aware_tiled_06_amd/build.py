@@ -42,7 +42,8 @@ HIPCC_FLAGS = [
 # Per-source code-generation flags. The forward kernels are scheduled with the
 # backend's maximum-ILP strategy: same instructions in another order (outputs
 # bitwise equal), measured 2.7-4.1 % faster on the 4096, 10,000 and 32K
-# workloads, causal and not.
+# workloads, causal and not. (flash_bwd.hip measured 1-6 % slower with it and
+# keeps the default.)
 SOURCE_FLAGS = {
     "flash_fwd.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
 }
