@@ -38,13 +38,15 @@ namespace {
 constexpr float kLazyRescale = 8.0f;  // log2 units
 // Operands of the next step's products read one step early: the first
 // FA_FWD_KP K operands of the score product and the first FA_FWD_VP V^T
-// operands of the P V product (tunable at build time; at d = 128 these
-// values keep every variant within 256 registers without spills).
+// operands of the P V product (tunable at build time). With the maximum-ILP
+// schedule the build uses, one K and two V^T operands measured fastest at the
+// 10,000 and 32K workloads (about 1 % over two and four; four and five V^T
+// operands, or two to four K operands, were slower).
 #ifndef FA_FWD_VP
-#define FA_FWD_VP 4
+#define FA_FWD_VP 2
 #endif
 #ifndef FA_FWD_KP
-#define FA_FWD_KP 2
+#define FA_FWD_KP 1
 #endif
 
 struct FwdParams {
