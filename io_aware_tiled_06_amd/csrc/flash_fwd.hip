@@ -142,14 +142,15 @@ __device__ __forceinline__ bool update_max(float m_tile, float& m_run, float& l_
 // start each step without waiting on LDS.
 //
 // Running maximum: tile t's probabilities are first computed with m as it
-// stands. If every lane's sum of its 16 probabilities is at most 2^8, every
-// probability is at most 2^8 (they are non-negative) and the tile is done:
+// stands. If every lane's sum of its 16 probabilities is at most 2^12, every
+// probability is at most 2^12 (they are non-negative) and the tile is done:
 // no row maximum is taken. Otherwise (in practice the tiles where a row's
 // scores jump by several units) the tile's exact maximum is found, m, the
 // running sum and the accumulator are rescaled by 2^(m_old - m_new), and the
 // tile's probabilities are recomputed, now at most 1. m therefore never
 // exceeds the running maximum and trails it by a bounded amount; P stays
-// inside the range of fp16 and bf16.
+// inside the range of fp16 (65504) and bf16. (A limit of 2^12 rather than 2^8
+// measured 1 % faster at 32K and 2 % causal: fewer tiles take the maximum.)
 //
 // Small grids (SPLIT = 2): when there are fewer query tiles than two per CU,
 // one wave per SIMD would be all the chip runs. The workgroup then has two
@@ -171,7 +172,7 @@ void flash_fwd_half(FwdParams p) {
   constexpr int DB = D / 32;  // 32-feature blocks of the output
   constexpr int kTile = BC * RB;
   constexpr int kPer = kTile / 1024 / NW;  // 1 KB direct copies per wave per tile
-  constexpr float kSumLimit = 256.f;       // per lane and tile, see above
+  constexpr float kSumLimit = 4096.f;      // per lane and tile, see above
   static_assert(kTile % (1024 * NW) == 0, "a tile must split into 1 KB copies evenly over the waves");
   using Swz = TileSwizzle<D>;
   __shared__ __attribute__((aligned(1024))) char smem[SPLIT * 2 * NBUF * kTile];  // per group: K ring, V ring
