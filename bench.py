@@ -224,8 +224,9 @@ class ClockSampler:
 
 def time_forward(name: str, steps: int = 20, warmup: int = 5) -> dict:
     """Kernel time of the fused forward pass on another named workload (HIP
-    events on the launch stream, as for the main line): the metric names both
-    the 4096- and the 32768-token cases."""
+    events on the launch stream around each launch, the launches queued
+    back to back): the metric names both the 4096- and the 32768-token
+    cases."""
     import numpy as np
     import torch
 
@@ -243,6 +244,11 @@ def time_forward(name: str, steps: int = 20, warmup: int = 5) -> dict:
     stream = torch.cuda.current_stream(dev)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     torch.cuda.synchronize(dev)
+    # A 0.07 ms launch is shorter than the host's time to issue an event and a
+    # launch, so the device would idle inside some event pairs. A spin kernel
+    # (about 10 ms) holds the stream while all launches and events are queued;
+    # the pairs then bracket back-to-back launches only.
+    torch.cuda._sleep(20_000_000)
     for a, b in ev:
         a.record(stream)
         fa.flash_attn_fwd(tq, tk, tv, w.scale, out=o)
