@@ -185,6 +185,40 @@ def test_constant_values(dtype):
     assert np.max(np.abs(o - v[:, :, :1, :])) <= MAX_ABS[dtype]
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("order", ["increasing", "decreasing", "spike"])
+def test_running_maximum_paths(order, dtype, causal):
+    """Scores whose row maximum moves across key tiles, against the oracle.
+
+    The kernel rescales only when a tile's probabilities, formed with the
+    running maximum as it stands, would exceed 2^12 per lane.
+    - increasing: key rows scaled by 1 + 3 j / N. The maximum climbs tile by
+      tile, and many tiles take the exact maximum and rescale.
+    - decreasing: the reverse. The first tile sets the maximum and no later
+      tile rescales.
+    - spike: one key in the middle scaled by 8. For many rows that key's
+      score jumps far beyond 2^12 over the running maximum.
+    Rows are rounded to the element type before both sides see them."""
+    from io_aware_tiled_06_amd.workloads import round_to_dtype
+
+    w = Workload("rescale", 1, 2, 2048, 128, dtype, 11)
+    q, k, v = make_inputs(w)
+    n = w.N
+    if order == "spike":
+        f = np.ones(n, dtype=np.float32)
+        f[n // 2 + 5] = 8.0
+    else:
+        f = 1.0 + 3.0 * np.arange(n, dtype=np.float32) / n
+        if order == "decreasing":
+            f = f[::-1].copy()
+    k = round_to_dtype(k * f[None, None, :, None], dtype)
+    print(f"[parity] running maximum {order} {dtype} causal={causal}", flush=True)
+    o, lse = run(lambda *a: fa.flash_attn_fwd(*a, causal=causal), q, k, v, dtype, w.scale)
+    o_ref, lse_ref = attention_reference(q, k, v, w.scale, causal=causal)
+    assert_close(o, lse, o_ref, lse_ref, dtype, f"running maximum {order}")
+
+
 def test_deterministic():
     w = WORKLOADS["n10000_d128_fp16"].with_(H=2)
     q, k, v = make_inputs(w)
