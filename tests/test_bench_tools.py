@@ -1,5 +1,10 @@
-"""bench.py's clock sampler reads the driver's sysfs files correctly (CPU only:
-a fake sysfs tree stands in for the card)."""
+"""bench.py's host-side tools, on the CPU:
+
+- the clock sampler reads the driver's sysfs files correctly (a fake sysfs
+  tree stands in for the card);
+- the traffic record is computed correctly from rocprofv3 counter files
+  (synthetic files stand in for a profiled run).
+"""
 import os
 import time
 
