@@ -206,6 +206,19 @@ def flash_attn_bwd(q, k, v, o, lse, dout, scale=None, *, causal=False, dq=None, 
     return dq, dk, dv
 
 
+def _check_workspace(workspace, device) -> None:
+    """A caller's workspace must be a contiguous tensor on the inputs' GPU: its
+    address is handed to the kernels, which write S and P through it."""
+    import torch
+
+    if not isinstance(workspace, torch.Tensor):
+        raise TypeError("workspace must be a torch.Tensor")
+    if workspace.device != device:
+        raise ValueError(f"workspace must be on the inputs' device {device} (got {workspace.device})")
+    if not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+
+
 def attn_naive_workspace_bytes(B: int, H: int, N: int, dtype: str) -> int:
     """Workspace for the three-pass path to process all heads at once."""
     return int(lib().attn_naive_workspace_bytes(B, H, N, DTYPE_CODE[dtype]))
@@ -227,6 +240,7 @@ def attn_naive_fwd(q, k, v, scale=None, *, out=None, return_lse=True, workspace=
     if workspace is None:
         nbytes = int(lib().attn_naive_workspace_bytes(B, H, N, _dtype_code(q)))
         workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    _check_workspace(workspace, q.device)
     ws_bytes = workspace.numel() * workspace.element_size()
     with torch.cuda.device(q.device):
         st = lib().attn_naive_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),

@@ -504,8 +504,9 @@ void flash_fwd_half(FwdParams p) {
     m_run = m_new;
   }
 
-  // Epilogue: one division per row ("rescale once at the end"), O rounded to
-  // nearest even; LSE = ln(2^m * l) = (m + log2 l) * ln 2.
+  // Epilogue: each row is divided by its sum l once, after the last tile
+  // ("FlashAttention, simplified", "The trick"); O rounded to nearest even;
+  // LSE = ln(2^m * l) = (m + log2 l) * ln 2.
   const float l_tot = pair_sum(l_run);
   const float inv = 1.f / l_tot;
   if (q_row < N) {

@@ -137,22 +137,53 @@ def attention_probabilities(q, k, scale: float, causal: bool = False):
     return e / e.sum(axis=-1, keepdims=True)
 
 
+def _block_partial(scores, v_blk):
+    """Softmax state of one block of keys on its own, per query row.
+
+    Returns (m_b, l_b, acc_b): the row maximum of the block's scores, the sum
+    of exp(score - m_b) over the block, and those same exponentials times the
+    block's value rows. A row that sees no key of the block (every score -inf,
+    causal only) gets m_b = -inf, l_b = 0 and acc_b = 0.
+    """
+    m_b = scores.max(axis=1)
+    shift = np.where(np.isfinite(m_b), m_b, 0.0)
+    e = np.exp(scores - shift[:, None])  # exp(-inf) = 0 for hidden keys
+    return m_b, e.sum(axis=1), e @ v_blk
+
+
+def _merge_partial(m, l, acc, m_b, l_b, acc_b):
+    """Fold one block's softmax state into the running state of the rows.
+
+    Both states are re-expressed relative to the larger of the two maxima:
+    the running sum and accumulator are multiplied by exp(m - m_new), which
+    is 1 unless the block raised the maximum, and the block's by
+    exp(m_b - m_new). The result is the state of the union of the two key
+    sets, exactly (up to rounding).
+    """
+    m_new = np.maximum(m, m_b)
+    ref = np.where(np.isfinite(m_new), m_new, 0.0)
+    a = np.where(np.isfinite(m), np.exp(m - ref), 0.0)
+    b = np.where(np.isfinite(m_b), np.exp(m_b - ref), 0.0)
+    return m_new, a * l + b * l_b, a[:, None] * acc + b[:, None] * acc_b
+
+
 def attention_online(q, k, v, scale: float, block: int, causal: bool = False):
     """The pages' streaming algorithm over K/V blocks, in float64.
 
-    "FlashAttention, simplified", "The trick": starting from m = -inf, l = 0,
-    acc = 0, for each block of ``block`` consecutive keys (the last one may be
-    shorter):
-        S     = scale * q k_blk^T
-        m_new = max(m, rowmax(S))
-        alpha = exp(m - m_new)
-        l     = alpha * l + rowsum(exp(S - m_new))
-        acc   = alpha * acc + exp(S - m_new) v_blk
-        m     = m_new
-    and finally O = acc / l.  LSE = m + ln l (the same reading as above).
+    "FlashAttention, simplified", "The trick": keys are visited one block at a
+    time while each query row carries a running maximum m (starting at -inf),
+    a running sum l of exponentials (starting at 0) and an unnormalised output
+    accumulator (starting at 0). Each block's scores are formed, the running
+    state is rescaled by exp(m_old - m_new) when the block raises the maximum,
+    the block's exponentials and their weighted values are added, and after
+    the last block the accumulator is divided by l once. Here a block's own
+    softmax state is formed first (``_block_partial``) and then folded into
+    the running state (``_merge_partial``), which is the same update written
+    as an exact merge of two partial softmaxes. ``block`` keys per block; the
+    last block may be shorter. LSE = m + ln l (the same reading as above).
     All query rows are carried together: query rows never interact.
-    causal=True: scores of keys j > i are -inf in every block (they add
-    exp(-inf) = 0); block 0 holds key 0, so no row starts from an empty block.
+    causal=True: scores of keys j > i are -inf in every block; block 0 holds
+    key 0, so every row has a finite maximum after the first block.
     Returns (O, LSE) like ``attention_reference``.
     """
     if block < 1:
@@ -178,12 +209,7 @@ def attention_online(q, k, v, scale: float, block: int, causal: bool = False):
             scores = s * (qh @ kh[j0:j1].T)
             if causal:
                 scores[np.arange(j0, j1)[None, :] > np.arange(nq)[:, None]] = -np.inf
-            m_new = np.maximum(m, scores.max(axis=1))
-            alpha = np.exp(m - m_new)
-            e = np.exp(scores - m_new[:, None])
-            l = alpha * l + e.sum(axis=1)
-            acc = alpha[:, None] * acc + e @ vh[j0:j1]
-            m = m_new
+            m, l, acc = _merge_partial(m, l, acc, *_block_partial(scores, vh[j0:j1]))
         out[idx] = acc / l[:, None]
         lse[idx] = m + np.log(l)
     return out, lse
@@ -268,3 +294,55 @@ def attention_backward_rows(q, k, v, do, scale: float, rows, causal: bool = Fals
             delta = p @ dp
             out[idx + (t,)] = s * ((p * (dp - delta)) @ kh[:end])
     return out
+
+
+def attention_backward_cols(q, k, v, do, scale: float, cols, causal: bool = False):
+    """dK and dV of attention for the key rows `cols` only, float64.
+
+    Key j's gradients gather over every query row that sees it:
+        dV_j = sum_i P_ij dO_i
+        dK_j = scale * sum_i P_ij (dP_ij - D_i) q_i
+    with P_ij the softmax of row i (over all N keys, or keys <= i when causal),
+    dP_ij = dO_i . v_j and D_i = sum_j' P_ij' dP_ij'. P_ij and D_i depend on
+    all of row i, so every query row is evaluated in full (in blocks of
+    complete rows, as in ``attention_reference``), but only the chosen
+    columns of P and dS are kept. The same chain rule as
+    ``attention_backward_reference``, organised so that it fits very long
+    sequences: the work is that of the forward definition, the memory one
+    block of rows.
+
+    q, k [..., N, d], v, do [..., N, dv]; cols: key indices. Returns
+    (dK [..., len(cols), d], dV [..., len(cols), dv]), float64.
+    """
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    _check(q, k, v)
+    if do.shape != q.shape[:-1] + (v.shape[-1],):
+        raise ValueError("do must have the shape of the output")
+    nq, nk = q.shape[-2], k.shape[-2]
+    if causal and nq != nk:
+        raise ValueError("causal attention needs as many queries as keys")
+    cols = np.asarray([int(j) for j in cols], dtype=np.int64)
+    if cols.size and (cols.min() < 0 or cols.max() >= nk):
+        raise ValueError("key index out of range")
+    s = np.float64(scale)
+    lead = q.shape[:-2]
+    dk = np.zeros(lead + (cols.size, q.shape[-1]), dtype=np.float64)
+    dv = np.zeros(lead + (cols.size, v.shape[-1]), dtype=np.float64)
+    rows = max(1, _BLOCK_BYTES // max(1, 16 * nk))  # two N-wide float64 blocks
+    for idx in np.ndindex(*lead):
+        qh, kh, vh, doh = q[idx], k[idx], v[idx], do[idx]
+        for r0 in range(0, nq, rows):
+            r1 = min(nq, r0 + rows)
+            scores = s * (qh[r0:r1] @ kh.T)
+            if causal:
+                scores[_future(r0, r1, nk)] = -np.inf
+            e = np.exp(scores - scores.max(axis=1, keepdims=True))
+            p = e / e.sum(axis=1, keepdims=True)
+            dp = doh[r0:r1] @ vh.T
+            delta = (p * dp).sum(axis=1, keepdims=True)
+            p_c = p[:, cols]
+            ds_c = p_c * (dp[:, cols] - delta)
+            dv[idx] += p_c.T @ doh[r0:r1]
+            dk[idx] += s * (ds_c.T @ qh[r0:r1])
+    return dk, dv
+

@@ -483,3 +483,20 @@ BWD_PINS = [
     pin_bwd_key_shift,
     pin_bwd_causal_future,
 ]
+
+
+def pin_bwd_cols_subset(cols_fn):
+    """A column-wise gradient (cols_fn(q, k, v, do, scale, cols, causal) ->
+    (dK rows, dV rows)) of a few keys, in any order, equals those keys' rows of
+    the same function over every key: each key's gradient is a sum over all
+    query rows, whose softmax runs over every key the row sees, not only the
+    chosen ones."""
+    rng = _rng(407)
+    q, k, v, do = (2.0 * rng.standard_normal((2, 45, 8)) for _ in range(4))
+    for causal in (False, True):
+        dk_all, dv_all = cols_fn(q, k, v, do, 0.55, range(45), causal)
+        pick = [44, 3, 0, 21]
+        dk, dv = cols_fn(q, k, v, do, 0.55, pick, causal)
+        assert np.max(np.abs(dk - dk_all[:, pick])) <= 1e-13 * max(1.0, np.max(np.abs(dk_all)))
+        assert np.max(np.abs(dv - dv_all[:, pick])) <= 1e-13 * max(1.0, np.max(np.abs(dv_all)))
+

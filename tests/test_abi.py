@@ -126,6 +126,24 @@ def test_binding_refuses_cpu_tensors():
         fa.attn_naive_fwd(x, x, x)
 
 
+def test_binding_refuses_bad_naive_workspace():
+    """The three-pass path writes S and P through the workspace address: a
+    workspace on the host (or another device), or a strided one, must raise
+    before any call."""
+    torch = pytest.importorskip("torch")
+    gpu = torch.device("cuda:0")  # a device object only; nothing is allocated on it
+    with pytest.raises(ValueError, match="device"):
+        fa._check_workspace(torch.empty(64, dtype=torch.uint8), gpu)
+    with pytest.raises(ValueError, match="device"):
+        fa._check_workspace(torch.empty(64, dtype=torch.uint8), torch.device("cuda:1"))
+    with pytest.raises(TypeError):
+        fa._check_workspace(bytearray(64), gpu)
+    strided = torch.empty(128, dtype=torch.uint8)[::2]
+    with pytest.raises(ValueError, match="contiguous"):
+        fa._check_workspace(strided, strided.device)
+    fa._check_workspace(torch.empty(64, dtype=torch.uint8), torch.device("cpu"))  # accepted as such
+
+
 def bwd(L, ptrs=None, B=1, H=1, N=16, d=64, scale=0.125, dtype=2, causal=False):
     base = [P, P2, P3, 0x70000, 0x80000, PL, 0x90000, 0xA0000, 0xB0000, 0xC0000]
     if ptrs:

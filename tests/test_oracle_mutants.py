@@ -68,6 +68,9 @@ def _mutant(q, k, v, scale, mutation):
 
 
 def _online_mutant(q, k, v, s, mutation, block):
+    """The streaming form as a merge of per-block softmax states (running
+    state rescaled by exp(m - m_new), the block's by exp(m_b - m_new)), with
+    one planted mistake."""
     lead = q.shape[:-2]
     nq, nk, dv = q.shape[-2], k.shape[-2], v.shape[-1]
     out = np.empty(lead + (nq, dv))
@@ -80,17 +83,16 @@ def _online_mutant(q, k, v, s, mutation, block):
         for j0 in range(0, stop, block):
             j1 = min(nk, j0 + block)
             sc = s * (q[idx] @ k[idx][j0:j1].T)
-            if mutation == "online_stale_max":
-                m_new = np.maximum(m, sc[:, 0])  # only looks at the first key
-            else:
-                m_new = np.maximum(m, sc.max(axis=1))
+            m_b = sc[:, 0] if mutation == "online_stale_max" else sc.max(axis=1)  # stale: first key only
+            e = np.exp(sc - m_b[:, None])
+            l_b, acc_b = e.sum(axis=1), e @ v[idx][j0:j1]
+            m_new = np.maximum(m, m_b)
+            a = np.exp(m - m_new)  # 0 on the first block (m = -inf)
             if mutation == "online_alpha_inverted":
-                alpha = np.exp(np.where(np.isfinite(m), m_new - m, -np.inf))
-            else:
-                alpha = np.exp(m - m_new)
-            e = np.exp(sc - m_new[:, None])
-            l = (l if mutation == "online_no_rescale_sum" else alpha * l) + e.sum(axis=1)
-            acc = (acc if mutation == "online_no_rescale_acc" else alpha[:, None] * acc) + e @ v[idx][j0:j1]
+                a = np.where(np.isfinite(m), np.exp(m_new - m), 0.0)
+            b = np.exp(m_b - m_new)
+            l = (l if mutation == "online_no_rescale_sum" else a * l) + b * l_b
+            acc = (acc if mutation == "online_no_rescale_acc" else a[:, None] * acc) + b[:, None] * acc_b
             m = m_new
         out[idx] = acc / l[:, None]
         lse[idx] = m + np.log(l)
@@ -201,3 +203,75 @@ def _bwd_mutant(q, k, v, do, scale, causal, mutation):
 def test_backward_mutant_is_caught(mutation):
     bad = failing_pins(lambda *a: _bwd_mutant(*a, mutation), BWD_PINS)
     assert bad, f"backward mutation {mutation} passed every backward pin"
+
+
+# -- column-wise dK, dV mistakes ---------------------------------------------------
+
+from oracle import attention_backward_rows  # noqa: E402
+from pins import pin_bwd_cols_subset  # noqa: E402
+
+COLS_MUTATIONS = ["normalise_over_chosen", "no_delta", "delta_over_chosen", "dk_no_scale", "causal_mask_dropped",
+                  "drop_last_row_block", "dv_uses_ds"]
+
+
+def _cols_mutant(q, k, v, do, scale, cols, causal, mutation, rows_per_block=16):
+    """Column-wise dK, dV over row blocks of complete rows, one planted mistake."""
+    q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
+    s = float(scale)
+    cols = np.asarray(list(cols), dtype=np.int64)
+    n = q.shape[-2]
+    dk = np.zeros(q.shape[:-2] + (cols.size, q.shape[-1]))
+    dv = np.zeros(q.shape[:-2] + (cols.size, v.shape[-1]))
+    starts = list(range(0, n, rows_per_block))
+    if mutation == "drop_last_row_block" and len(starts) > 1:
+        starts = starts[:-1]
+    for idx in np.ndindex(*q.shape[:-2]):
+        for r0 in starts:
+            r1 = min(n, r0 + rows_per_block)
+            sc = s * (q[idx][r0:r1] @ k[idx].T)
+            if causal and mutation != "causal_mask_dropped":
+                sc = np.where(np.arange(n)[None, :] > np.arange(r0, r1)[:, None], -np.inf, sc)
+            if mutation == "normalise_over_chosen":
+                e = np.exp(sc[:, cols] - sc[:, cols].max(axis=1, keepdims=True))
+                p_c = e / e.sum(axis=1, keepdims=True)
+                p = None
+            else:
+                e = np.exp(sc - sc.max(axis=1, keepdims=True))
+                p = e / e.sum(axis=1, keepdims=True)
+                p_c = p[:, cols]
+            dp = do[idx][r0:r1] @ v[idx].T
+            if mutation == "no_delta":
+                delta = 0.0
+            elif mutation in ("delta_over_chosen", "normalise_over_chosen"):
+                delta = (p_c * dp[:, cols]).sum(axis=1, keepdims=True)
+            else:
+                delta = (p * dp).sum(axis=1, keepdims=True)
+            ds_c = p_c * (dp[:, cols] - delta)
+            dv[idx] += (ds_c if mutation == "dv_uses_ds" else p_c).T @ do[idx][r0:r1]
+            dk[idx] += (1.0 if mutation == "dk_no_scale" else s) * (ds_c.T @ q[idx][r0:r1])
+    return dk, dv
+
+
+def _failing_cols_pins(cols_fn):
+    def bwd(q, k, v, do, scale, causal):
+        n = np.asarray(q).shape[-2]
+        dk, dv = cols_fn(q, k, v, do, scale, range(n), causal)
+        return attention_backward_rows(q, k, v, do, scale, range(n), causal=causal), dk, dv
+
+    bad = failing_pins(bwd, BWD_PINS)
+    try:
+        with np.errstate(all="ignore"):
+            pin_bwd_cols_subset(cols_fn)
+    except Exception:  # noqa: BLE001 - any failure counts
+        bad.append("pin_bwd_cols_subset")
+    return bad
+
+
+@pytest.mark.parametrize("mutation", COLS_MUTATIONS)
+def test_cols_mutant_is_caught(mutation):
+    bad = _failing_cols_pins(lambda *a: _cols_mutant(*a, mutation))
+    assert bad, f"column-wise mutation {mutation} passed every pin"
+
+
+def test_cols_mutant_harness_is_sound():
+    assert _failing_cols_pins(lambda *a: _cols_mutant(*a, "none")) == []

@@ -203,3 +203,68 @@ def test_backward_rows_closed_forms():
         full = attention_backward_reference(q, k, v, do, 0.45, causal=causal)[0]
         got = attention_backward_rows(q, k, v, do, 0.45, [3, 0, 29], causal=causal)
         assert np.max(np.abs(got - full[:, [3, 0, 29]])) <= 1e-13
+
+
+# -- column-wise dK, dV (long sequences) -------------------------------------------
+
+from oracle import attention_backward_cols  # noqa: E402
+from pins import BWD_PINS, pin_bwd_cols_subset  # noqa: E402
+
+
+def _bwd_via_cols(q, k, v, do, scale, causal):
+    """(dQ, dK, dV) with dK and dV from the column-wise function over every key
+    (dQ from the separately pinned row-wise function), so that every backward
+    pin applies to the column-wise gradients."""
+    n = np.asarray(q).shape[-2]
+    dk, dv = attention_backward_cols(q, k, v, do, scale, range(n), causal=causal)
+    return attention_backward_rows(q, k, v, do, scale, range(n), causal=causal), dk, dv
+
+
+@pytest.mark.parametrize("pin", BWD_PINS, ids=lambda p: p.__name__)
+def test_backward_cols_backward_pins(pin):
+    pin(_bwd_via_cols)
+
+
+def test_backward_cols_subset():
+    pin_bwd_cols_subset(attention_backward_cols)
+
+
+def test_backward_cols_against_library_autograd():
+    """torch's float64 autograd through its own CPU attention, sampled keys."""
+    import torch
+    import torch.nn.functional as F
+
+    rng = np.random.default_rng(420)
+    for causal in (False, True):
+        q, k, v, do = (rng.standard_normal((2, 3, 57, 16)) for _ in range(4))
+        scale = 0.3
+        cols = [0, 1, 20, 55, 56]
+        dk, dv = attention_backward_cols(q, k, v, do, scale, cols, causal=causal)
+        tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+        o = F.scaled_dot_product_attention(tq, tk, tv, scale=scale, is_causal=causal)
+        o.backward(torch.from_numpy(do))
+        assert np.max(np.abs(dk - tk.grad.numpy()[:, :, cols])) <= 1e-12, causal
+        assert np.max(np.abs(dv - tv.grad.numpy()[:, :, cols])) <= 1e-12, causal
+
+
+def test_backward_cols_row_blocks(monkeypatch):
+    """Rows are gathered in blocks of complete rows (the last one ragged): the
+    sums over blocks equal the full-matrix gradient's columns."""
+    import oracle.attention as oa
+
+    rng = np.random.default_rng(421)
+    q, k, v, do = (1.5 * rng.standard_normal((2, 100, 8)) for _ in range(4))
+    monkeypatch.setattr(oa, "_BLOCK_BYTES", 16 * 100 * 7)  # seven rows per block
+    for causal in (False, True):
+        full = attention_backward_reference(q, k, v, do, 0.6, causal=causal)
+        dk, dv = attention_backward_cols(q, k, v, do, 0.6, [99, 0, 31, 64], causal=causal)
+        assert np.max(np.abs(dk - full[1][:, [99, 0, 31, 64]])) <= 1e-13
+        assert np.max(np.abs(dv - full[2][:, [99, 0, 31, 64]])) <= 1e-13
+
+
+def test_backward_cols_rejects_bad_keys():
+    x = np.zeros((1, 4, 2))
+    with pytest.raises(ValueError):
+        attention_backward_cols(x, x, x, x, 1.0, [4])
+    with pytest.raises(ValueError):
+        attention_backward_cols(x, x, x, x, 1.0, [-1])
