@@ -35,9 +35,11 @@
  * Streams: `stream` is a hipStream_t passed as void*; NULL selects the null
  * stream. Kernels are launched on the calling thread's current HIP device,
  * and `stream` must belong to that device. Calls are asynchronous on that
- * stream and never synchronise. The library holds no per-call state (only a
- * per-device cache of the compute-unit count, read on first use), so calls
- * from several host threads are safe.
+ * stream and never synchronise. The library holds no per-call state (only
+ * per-device caches of the compute-unit count and of the address of
+ * flash_attn_bwd_noalloc's fixed scratch, each filled on first use), so calls
+ * from several host threads are safe, except overlapping calls of
+ * flash_attn_bwd_noalloc on one device (see there).
  */
 #ifndef FLASH_ATTN_H
 #define FLASH_ATTN_H
@@ -58,7 +60,8 @@ typedef enum {
   FA_ERR_ALIGN = 4,       /* a base pointer is not 16-byte aligned          */
   FA_ERR_WORKSPACE = 5,   /* naive path: workspace smaller than one head    */
   FA_ERR_SCALE = 6,       /* scale is NaN or infinite                       */
-  FA_ERR_HIP = 7          /* the HIP runtime reported an error at launch    */
+  FA_ERR_HIP = 7,         /* the HIP runtime reported an error at launch    */
+  FA_ERR_TOO_LARGE = 8    /* flash_attn_bwd_noalloc: B*H*N > FA_NOALLOC_MAX_ROWS */
 } fa_status;
 
 /*
@@ -133,6 +136,28 @@ int flash_attn_bwd(const void* q, const void* k, const void* v, const void* o, c
 int flash_attn_bwd_causal(const void* q, const void* k, const void* v, const void* o, const void* dout,
                           const float* lse, void* dq, void* dk, void* dv, float* delta,
                           int B, int H, int N, int d, float scale, int dtype, void* stream);
+
+/*
+ * flash_attn_bwd_noalloc -- flash_attn_bwd without the caller's `delta`
+ * scratch, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation). The
+ * library keeps the 2*B*H*N floats of row statistics in a fixed device array
+ * of FA_NOALLOC_MAX_ROWS * 2 floats (32 MiB), one per device, held from the
+ * library's load until the process ends; the call allocates and frees nothing.
+ * Its device address is looked up on the first call on each device.
+ *
+ * Arguments, layout, arithmetic, results and status codes as flash_attn_bwd
+ * (non-causal), minus `delta`; gradients are bitwise those of flash_attn_bwd.
+ * B*H*N above FA_NOALLOC_MAX_ROWS returns FA_ERR_TOO_LARGE before any HIP
+ * call. Every call on one device shares that device's array and overwrites it
+ * before reading it: calls that overlap on one device (on different streams,
+ * or from several host threads without ordering) race and may return wrong
+ * gradients. Calls ordered on one stream are safe.
+ */
+#define FA_NOALLOC_MAX_ROWS 4194304
+int flash_attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                           const float* lse, void* dq, void* dk, void* dv,
+                           int B, int H, int N, int d, float scale, int dtype, void* stream);
 
 /*
  * attn_naive_workspace_bytes -- workspace for attn_naive_fwd to process every

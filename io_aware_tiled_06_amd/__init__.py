@@ -32,15 +32,21 @@ __all__ = [
     "FA_ERR_WORKSPACE",
     "FA_ERR_SCALE",
     "FA_ERR_HIP",
+    "FA_ERR_TOO_LARGE",
+    "NOALLOC_MAX_ROWS",
+    "flash_attn_bwd_noalloc",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libflashattn.so")
 EXPORTED_SYMBOLS = ("flash_attn_fwd", "flash_attn_fwd_causal", "flash_attn_bwd", "flash_attn_bwd_causal",
-                    "attn_naive_workspace_bytes", "attn_naive_fwd", "fa_strerror")
+                    "flash_attn_bwd_noalloc", "attn_naive_workspace_bytes", "attn_naive_fwd", "fa_strerror")
 
 # fa_status values (include/flash_attn.h)
 FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED = 0, 1, 2, 3
 FA_ERR_ALIGN, FA_ERR_WORKSPACE, FA_ERR_SCALE, FA_ERR_HIP = 4, 5, 6, 7
+FA_ERR_TOO_LARGE = 8
+# largest B*H*N of flash_attn_bwd_noalloc (FA_NOALLOC_MAX_ROWS)
+NOALLOC_MAX_ROWS = 4194304
 # fa_dtype values
 DTYPE_CODE = {"fp32": 0, "fp16": 1, "bf16": 2}
 
@@ -72,6 +78,8 @@ def lib() -> ctypes.CDLL:
             fn = getattr(L, name)
             fn.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
             fn.restype = i
+        L.flash_attn_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
+        L.flash_attn_bwd_noalloc.restype = i
         L.attn_naive_workspace_bytes.argtypes = [i, i, i, i]
         L.attn_naive_workspace_bytes.restype = sz
         L.attn_naive_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, sz, vp]
@@ -203,6 +211,31 @@ def flash_attn_bwd(q, k, v, o, lse, dout, scale=None, *, causal=False, dq=None, 
                 _stream_ptr(q, stream))
     if st != FA_OK:
         raise FlashAttnError(st, "flash_attn_bwd_causal" if causal else "flash_attn_bwd")
+    return dq, dk, dv
+
+
+def flash_attn_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, scale=None, *, stream=None):
+    """flash_attn_bwd (non-causal) through the entry point that allocates
+    nothing: the row statistics live in the library's fixed device scratch
+    (B*H*N <= NOALLOC_MAX_ROWS). The caller supplies every output (dq, dk, dv
+    like q). Calls that overlap on one GPU share that scratch and race."""
+    import torch
+
+    _check_inputs(q, k, v)
+    B, H, N, d = q.shape
+    for name, t in (("o", o), ("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv)):
+        if (not isinstance(t, torch.Tensor) or t.shape != q.shape or t.dtype != q.dtype or t.device != q.device
+                or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous tensor of q's shape, dtype and device")
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or lse.device != q.device or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor on q's device")
+    s = _default_scale(d) if scale is None else float(scale)
+    with torch.cuda.device(q.device):
+        st = lib().flash_attn_bwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+                                          lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, s,
+                                          _dtype_code(q), _stream_ptr(q, stream))
+    if st != FA_OK:
+        raise FlashAttnError(st, "flash_attn_bwd_noalloc")
     return dq, dk, dv
 
 

@@ -4,8 +4,18 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "flash_attn.h"
 #include "fa_launch.h"
+
+// Scratch of flash_attn_bwd_noalloc: the backward pass's row statistics (D,
+// then LSE * log2(e)), 2 * B * H * N floats, in a fixed device array instead of
+// a caller's buffer. Each device that loads the library holds its own copy
+// until the process ends. Host code never uses the name `scratch` as an
+// address (on the host it is only a stand-in for the device symbol): the
+// device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) float scratch[FA_NOALLOC_MAX_ROWS * 2];
 
 namespace {
 
@@ -52,6 +62,29 @@ fa::AttnArgs make_args(const void* q, const void* k, const void* v, void* o, flo
   return a;
 }
 
+// Device address of `scratch` on the current device, looked up once per device
+// (with that device current) and kept; nullptr if the lookup fails.
+float* scratch_ptr(hipError_t* err) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static float* ptr[kMaxDevices] = {};
+  int dev = 0;
+  *err = hipGetDevice(&dev);
+  if (*err != hipSuccess) return nullptr;
+  if (dev < 0 || dev >= kMaxDevices) {
+    *err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptr[dev]) {
+    void* p = nullptr;
+    *err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (*err != hipSuccess) return nullptr;
+    ptr[dev] = static_cast<float*>(p);
+  }
+  return ptr[dev];
+}
+
 // Bytes one head occupies in the three-pass workspace, or 0 on overflow.
 size_t naive_head_bytes(int N, int dtype) {
   const unsigned __int128 n = (unsigned)N;
@@ -81,15 +114,22 @@ int flash_attn_fwd_causal(const void* q, const void* k, const void* v, void* o, 
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
-static int flash_attn_bwd_impl(const void* q, const void* k, const void* v, const void* o, const void* dout,
-                               const float* lse, void* dq, void* dk, void* dv, float* delta, int B, int H, int N,
-                               int d, float scale, int dtype, void* stream, bool causal) {
-  bool empty;
-  const int st = validate(q, k, v, dq, lse, B, H, N, d, scale, dtype, &empty);
-  if (st != FA_OK || empty) return st;
-  if (!o || !dout || !lse || !dk || !dv || !delta) return FA_ERR_NULL;
-  if (!aligned16(o) || !aligned16(dout) || !aligned16(dk) || !aligned16(dv) || !aligned16(delta))
-    return FA_ERR_ALIGN;
+// Every check of the backward entry points except their row-statistics
+// scratch. Returns FA_OK with *empty set when there is nothing to compute.
+static int validate_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                        const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
+                        int dtype, bool* empty) {
+  const int st = validate(q, k, v, dq, lse, B, H, N, d, scale, dtype, empty);
+  if (st != FA_OK || *empty) return st;
+  if (!o || !dout || !lse || !dk || !dv) return FA_ERR_NULL;
+  if (!aligned16(o) || !aligned16(dout) || !aligned16(dk) || !aligned16(dv)) return FA_ERR_ALIGN;
+  return FA_OK;
+}
+
+// Launch of a validated backward pass with row-statistics scratch `delta`.
+static int launch_bwd_checked(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                              const float* lse, void* dq, void* dk, void* dv, float* delta, int B, int H, int N,
+                              int d, float scale, int dtype, void* stream, bool causal) {
   fa::BwdArgs a;
   a.q = q;
   a.k = k;
@@ -112,6 +152,17 @@ static int flash_attn_bwd_impl(const void* q, const void* k, const void* v, cons
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+static int flash_attn_bwd_impl(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                               const float* lse, void* dq, void* dk, void* dv, float* delta, int B, int H, int N,
+                               int d, float scale, int dtype, void* stream, bool causal) {
+  bool empty;
+  const int st = validate_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, dtype, &empty);
+  if (st != FA_OK || empty) return st;
+  if (!delta) return FA_ERR_NULL;
+  if (!aligned16(delta)) return FA_ERR_ALIGN;
+  return launch_bwd_checked(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N, d, scale, dtype, stream, causal);
+}
+
 int flash_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
                    void* dq, void* dk, void* dv, float* delta, int B, int H, int N, int d, float scale, int dtype,
                    void* stream) {
@@ -122,6 +173,21 @@ int flash_attn_bwd_causal(const void* q, const void* k, const void* v, const voi
                           const float* lse, void* dq, void* dk, void* dv, float* delta, int B, int H, int N, int d,
                           float scale, int dtype, void* stream) {
   return flash_attn_bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N, d, scale, dtype, stream, true);
+}
+
+int flash_attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                           const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
+                           int dtype, void* stream) {
+  // Every check of flash_attn_bwd except the caller's scratch pointer, then
+  // the size limit of the fixed scratch; all before any HIP call.
+  bool empty;
+  const int st = validate_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, dtype, &empty);
+  if (st != FA_OK || empty) return st;
+  if ((int64_t)B * H * N > FA_NOALLOC_MAX_ROWS) return FA_ERR_TOO_LARGE;
+  hipError_t e;
+  float* delta = scratch_ptr(&e);
+  if (!delta) return FA_ERR_HIP;
+  return launch_bwd_checked(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N, d, scale, dtype, stream, false);
 }
 
 size_t attn_naive_workspace_bytes(int B, int H, int N, int dtype) {
@@ -157,6 +223,7 @@ const char* fa_strerror(int status) {
     case FA_ERR_WORKSPACE: return "workspace smaller than one head";
     case FA_ERR_SCALE: return "scale is not finite";
     case FA_ERR_HIP: return "HIP launch error";
+    case FA_ERR_TOO_LARGE: return "B*H*N exceeds the fixed scratch of the allocation-free entry point";
     default: return "unknown status";
   }
 }

@@ -165,3 +165,32 @@ def test_backward_validation(L, causal):
         assert bwd(L, {i: [P, P2, P3, 0x70000, 0x80000, PL, 0x90000, 0xA0000, 0xB0000, 0xC0000][i] + 2},
                    causal=causal) == fa.FA_ERR_ALIGN, i
     assert bwd(L, N=0, causal=causal) == fa.FA_OK
+
+
+def bwd_noalloc(L, ptrs=None, B=1, H=1, N=16, d=64, scale=0.125, dtype=2):
+    base = [P, P2, P3, 0x70000, 0x80000, PL, 0x90000, 0xA0000, 0xB0000]
+    if ptrs:
+        for i, val in ptrs.items():
+            base[i] = val
+    return L.flash_attn_bwd_noalloc(*base, B, H, N, d, scale, dtype, None)
+
+
+def test_noalloc_backward_validation(L):
+    """The allocation-free backward pass validates like flash_attn_bwd and
+    rejects problems beyond its fixed scratch, all before any HIP call."""
+    assert bwd_noalloc(L, B=-1) == fa.FA_ERR_SHAPE
+    assert bwd_noalloc(L, d=96) == fa.FA_ERR_UNSUPPORTED
+    assert bwd_noalloc(L, dtype=7) == fa.FA_ERR_UNSUPPORTED
+    assert bwd_noalloc(L, scale=math.inf) == fa.FA_ERR_SCALE
+    for i in range(9):
+        assert bwd_noalloc(L, {i: None}) == fa.FA_ERR_NULL, i
+    for i in (0, 3, 4, 6, 7, 8):
+        assert bwd_noalloc(L, {i: [P, P2, P3, 0x70000, 0x80000, PL, 0x90000, 0xA0000, 0xB0000][i] + 2}) == \
+            fa.FA_ERR_ALIGN, i
+    assert bwd_noalloc(L, N=0) == fa.FA_OK
+    # one row past the limit, in several shapes
+    assert bwd_noalloc(L, B=1, H=1, N=fa.NOALLOC_MAX_ROWS + 1) == fa.FA_ERR_TOO_LARGE
+    assert bwd_noalloc(L, B=2, H=64, N=32769) == fa.FA_ERR_TOO_LARGE
+    assert bwd_noalloc(L, B=1 << 20, H=1 << 20, N=1 << 20) in (fa.FA_ERR_SHAPE, fa.FA_ERR_TOO_LARGE)
+    assert "scratch" in fa.strerror(fa.FA_ERR_TOO_LARGE)
+
