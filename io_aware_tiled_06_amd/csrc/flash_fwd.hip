@@ -152,6 +152,17 @@ __device__ __forceinline__ bool update_max(float m_tile, float& m_run, float& l_
 // inside the range of fp16 (65504) and bf16. (A limit of 2^12 rather than 2^8
 // measured 1 % faster at 32K and 2 % causal: fewer tiles take the maximum.)
 //
+// Normaliser of O (bf16 inputs): the probabilities enter the P V product
+// rounded to bf16 (8 significant bits), so O is divided by the sum of those
+// rounded values, l_r, while LSE keeps the sum of the unrounded ones, l. With
+// l the weights of a row would miss summing to 1 by the rounding of its
+// largest probabilities: on a row dominated by one key, O would be off by up
+// to |v| * 2^-9 on top of the rounding of O itself (half an ulp, 2^-6, at
+// |O| >= 4), which exceeded 2e-2 on the 32K workload's peaky rows. With l_r the weights
+// sum to 1 and a dominant key's value comes through unchanged; LSE needs the
+// unrounded sum (l_r would move it by up to 2^-9). For fp16 (11 bits) the
+// rounding is 8 times smaller and O is divided by l.
+//
 // Small grids (SPLIT = 2): when there are fewer query tiles than two per CU,
 // one wave per SIMD would be all the chip runs. The workgroup then has two
 // groups of NW waves over the same query rows; group 0 takes the first half
@@ -289,7 +300,28 @@ void flash_fwd_half(FwdParams p) {
   f32x16 acc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
-  float l_run = 0.f, m_run;
+  // l_run: this lane's share of the sum of the unrounded probabilities (for
+  // LSE). bf16 only: lr_acc, the sums of the rounded probabilities (the
+  // normaliser of O, see above), formed on the matrix cores. Per step and key
+  // half, v_mfma_f32_16x16x32_bf16 takes the probabilities as its B operand
+  // (lane l: query l % 32, 8 keys of lane group l / 16, the same registers as
+  // the P V product) and a constant 0/1 A operand whose row 0 selects the
+  // lane groups of queries 0-15 (0 and 2) and row 1 those of queries 16-31
+  // (1 and 3): output row 0, column n, is query n's sum over the half, row 1
+  // query n + 16's. Rows 0 and 1 sit in registers 0 and 1 of lanes 0-15.
+  // (The same sums on the vector ALU, one v_dot2 per pair, measured twice as
+  // costly: the kernel runs at a power-limited clock, 1.7 GHz, where every
+  // extra instruction shows.)
+  constexpr bool kRoundedSum = std::is_same<E, BF16>::value;
+  float l_run = 0.f, lr_run = 0.f, m_run;
+  f32x4 lr_acc = {};
+  bf16x8 sel_ones;
+  {
+    const int row = lane & 15, blk = lane >> 4;
+    const bool one = (row == 0 && (blk & 1) == 0) || (row == 1 && (blk & 1) == 1);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sel_ones[i] = one ? (__bf16)1.0f : (__bf16)0.0f;
+  }
   // hidden keys must lose the row extremum: -inf for c >= 0, +inf for c < 0
   constexpr float hide = NEG ? INFINITY : -INFINITY;
 
@@ -348,7 +380,8 @@ void flash_fwd_half(FwdParams p) {
 #pragma unroll
     for (int i = 0; i < VP; ++i) pre_v[i] = read_vt(vb_lds, i / 2, i % 2);
   };
-  // O^T += V^T P^T for one tile.
+  // O^T += V^T P^T for one tile (its first VP operands were read ahead by
+  // prefetch_v).
   auto accumulate = [&](const char* vb_lds, const u32x4(&pf)[2]) {
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -374,6 +407,14 @@ void flash_fwd_half(FwdParams p) {
     float lt = probs(s, pf, key0, mask);
     if (__any(!(lt <= kSumLimit))) {
       const float m_new = fmaxf(m_run, tile_max(s, key0, mask));
+      if constexpr (kRoundedSum) {
+        // every lane takes part: lanes 0-15 rescale the sums of queries
+        // lane and lane + 16, whose factors lanes lane and lane + 16 hold
+        const float a_all = m_new != m_run ? exp2_fast(m_run - m_new) : 1.f;
+        const float a_hi = __shfl(a_all, (lane & 15) + 16);
+        lr_acc[0] *= a_all;
+        lr_acc[1] *= a_hi;
+      }
       if (m_new != m_run) {
         const float alpha = exp2_fast(m_run - m_new);
 #pragma unroll
@@ -384,6 +425,11 @@ void flash_fwd_half(FwdParams p) {
       lt = probs(s, pf, key0, mask);
     }
     l_run += lt;
+    if constexpr (kRoundedSum) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        lr_acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel_ones, __builtin_bit_cast(bf16x8, pf[h]), lr_acc, 0, 0, 0);
+    }
   };
   // Tiles that need masking: the ragged last one, and (causal) the diagonal.
   auto needs_mask = [&](int t) { return kt0 + t == n_full || (CAUSAL && kt0 + t == diag); };
@@ -475,32 +521,39 @@ void flash_fwd_half(FwdParams p) {
   // the last barrier).
   if (last >= 0 && last == steps - 1) accumulate(vbuf(last % NBUF), pb[1]);
 
+  if constexpr (kRoundedSum) {
+    // the whole row's rounded sum, for this lane's query
+    const float s0 = __shfl(lr_acc[0], lane & 15), s1 = __shfl(lr_acc[1], lane & 15);
+    lr_run = (lane & 16) ? s1 : s0;
+  }
   if constexpr (SPLIT == 2) {
     // Group 1 hands (m, l, accumulator) to group 0 through LDS (the rings are
     // free once every wave has passed the barrier); lane-major per wave.
-    constexpr int kX = 2 + 16 * DB;
+    constexpr int kX = 3 + 16 * DB;
     static_assert(NW * kX * 64 * 4 <= SPLIT * 2 * NBUF * kTile, "exchange must fit in the rings");
     float* const xch = reinterpret_cast<float*>(smem) + wave * kX * 64 + lane;
     __syncthreads();
     if (grp == 1) {
       xch[0] = m_run;
       xch[64] = l_run;
+      xch[128] = lr_run;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) xch[(2 + db * 16 + r) * 64] = acc[db][r];
+        for (int r = 0; r < 16; ++r) xch[(3 + db * 16 + r) * 64] = acc[db][r];
     }
     __syncthreads();
     if (grp == 1) return;
-    const float m1 = xch[0], l1 = xch[64];
+    const float m1 = xch[0], l1 = xch[64], lr1 = xch[128];
     const float m_new = fmaxf(m_run, m1);
     const float a0 = m_run == m_new ? 1.f : exp2_fast(m_run - m_new);
     const float a1 = m1 == m_new ? 1.f : exp2_fast(m1 - m_new);
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[db][r] = a0 * acc[db][r] + a1 * xch[(2 + db * 16 + r) * 64];
+      for (int r = 0; r < 16; ++r) acc[db][r] = a0 * acc[db][r] + a1 * xch[(3 + db * 16 + r) * 64];
     l_run = a0 * l_run + a1 * l1;
+    if constexpr (kRoundedSum) lr_run = a0 * lr_run + a1 * lr1;
     m_run = m_new;
   }
 
@@ -508,7 +561,7 @@ void flash_fwd_half(FwdParams p) {
   // ("FlashAttention, simplified", "The trick"); O rounded to nearest even;
   // LSE = ln(2^m * l) = (m + log2 l) * ln 2.
   const float l_tot = pair_sum(l_run);
-  const float inv = 1.f / l_tot;
+  const float inv = 1.f / (kRoundedSum ? lr_run : l_tot);
   if (q_row < N) {
     char* orow = p.o + head + (int64_t)q_row * RB;
 #pragma unroll

@@ -32,7 +32,7 @@ torch = pytest.importorskip("torch")
 
 import io_aware_tiled_06_amd as fa  # noqa: E402
 from io_aware_tiled_06_amd.workloads import WORKLOADS, Workload, make_inputs, sample_rows  # noqa: E402
-from oracle import attention_backward_reference, attention_backward_rows  # noqa: E402
+from oracle import attention_backward_cols, attention_backward_reference, attention_backward_rows  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 
@@ -162,6 +162,8 @@ def test_backward_long_context(causal):
     in the launches `bench.py --backward` times.
 
     dQ: sampled rows against the row-wise oracle, to the bf16 bounds above.
+    dK, dV: one key of every 256-key tile of head 0 (and tile edges) against
+    the column-wise oracle, to the same bounds.
     dV: the identity sum_j dV_j = sum_i dO_i (every probability row sums to
     1, causal rows too), which holds at any size. Its error has two sources:
     the rounded probabilities of a row sum to 1 within about u/(2 sqrt 3)
@@ -191,6 +193,24 @@ def test_backward_long_context(causal):
     mx = float(np.max(np.abs(err)) / np.max(np.abs(ref)))
     print(f"[bwd] n32768 causal={causal} dQ rows: rel_rms={rel:.2e} rel_max={mx:.2e}", flush=True)
     assert rel <= rel_rms_tol and mx <= rel_max_tol
+
+    # dK and dV of head 0 at one key per 256-key workgroup tile (a different
+    # offset in each tile) plus tile edges, element by element against the
+    # column-wise oracle (every query row of the head gathered per key)
+    h = 0
+    cols = np.unique(np.concatenate([np.arange(0, w.N, 256) + (np.arange(w.N // 256) * 37) % 256,
+                                     [0, 31, 32, 255, 256, w.N - 1]]))
+    got_k = dk[0, h, torch.from_numpy(cols).cuda()].double().cpu().numpy()
+    got_v = dv[0, h, torch.from_numpy(cols).cuda()].double().cpu().numpy()
+    print(f"[bwd] n32768 causal={causal} dK/dV of {len(cols)} keys of head {h}: oracle", flush=True)
+    ref_k, ref_v = attention_backward_cols(q[:, h:h + 1], k[:, h:h + 1], v[:, h:h + 1], do[:, h:h + 1], w.scale,
+                                           cols, causal=causal)
+    for name, g, r in (("dK", got_k, ref_k[0, 0]), ("dV", got_v, ref_v[0, 0])):
+        e = g - r
+        rel = float(np.linalg.norm(e) / np.linalg.norm(r))
+        mx = float(np.max(np.abs(e)) / np.max(np.abs(r)))
+        print(f"[bwd] n32768 causal={causal} {name} keys: rel_rms={rel:.2e} rel_max={mx:.2e}", flush=True)
+        assert rel <= rel_rms_tol and mx <= rel_max_tol, name
 
     lhs = dv.double().sum(dim=2).cpu().numpy()
     rhs = do.astype(np.float64).sum(axis=2)

@@ -108,6 +108,29 @@ def test_long_context_sampled_rows(long_context):
         assert excess <= 2e-2, (h, excess)
 
 
+def test_long_context_full_heads(long_context):
+    """The benchmark's launch at full size (8-wave, 256-row workgroups), every
+    row of heads 0 and 15 compared element by element with the oracle: max|dO|
+    and max|dLSE| over all 2 x 32768 rows, and the relative RMS over those two
+    heads (also per head)."""
+    w, (q, k, v), (tq, tk, tv) = long_context
+    heads = [0, w.H - 1]
+    print(f"[parity] flash n32768_d128_bf16 full heads {heads}", flush=True)
+    o = torch.empty_like(tq)
+    o, lse = fa.flash_attn_fwd(tq, tk, tv, w.scale, out=o)  # exactly bench.py's call
+    torch.cuda.synchronize()
+    o_h = o[:, heads].float().cpu().numpy().astype(np.float64)
+    lse_h = lse[:, heads].cpu().numpy().astype(np.float64)
+    o_ref, lse_ref = attention_reference(q[:, heads], k[:, heads], v[:, heads], w.scale)
+    for i, h in enumerate(heads):
+        d = o_h[:, i] - o_ref[:, i]
+        print(f"[parity] head {h}: max|dO| {np.max(np.abs(d)):.3e} rel_rms "
+              f"{np.linalg.norm(d) / np.linalg.norm(o_ref[:, i]):.3e} max|dLSE| "
+              f"{np.max(np.abs(lse_h[:, i] - lse_ref[:, i])):.3e}", flush=True)
+        assert_close(o_h[:, i], lse_h[:, i], o_ref[:, i], lse_ref[:, i], w.dtype, f"n32768 head {h}")
+    assert_close(o_h, lse_h, o_ref, lse_ref, w.dtype, "n32768 heads 0 and 15")
+
+
 def test_long_context_naive_chunked(long_context):
     """Three-pass path at 32K with a workspace of 3 heads (chunks of 3,3,...,1)."""
     w, (q, k, v), (tq, tk, tv) = long_context
@@ -353,6 +376,32 @@ def test_wide_workgroups_ragged_sampled_rows(causal):
     else:
         o_ref, lse_ref = attention_reference(q[:, :, rows], k, v, w.scale)
     assert_close(o_s, lse_s, o_ref, lse_ref, w.dtype, f"wide N=8200 causal={causal}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_wide_workgroups_ragged_full_heads(causal):
+    """The 8-wave, 256-row launch on the ragged B=2, H=16, N=8200 grid: every
+    row of two heads (batch 0 head 0, batch 1 head 15: the first and the last
+    workgroups of the grid) against the oracle, causal and not."""
+    w = Workload("wide", 2, 16, 8200, 128, "bf16", 77, 3.0)
+    q, k, v = make_inputs(w)
+    tq, tk, tv = dev(q, w.dtype), dev(k, w.dtype), dev(v, w.dtype)
+    print(f"[parity] wide workgroups N=8200 full heads causal={causal}", flush=True)
+    o, lse = fa.flash_attn_fwd(tq, tk, tv, w.scale, causal=causal)
+    torch.cuda.synchronize()
+    for b, h in ((0, 0), (1, 15)):
+        o_h = o[b, h].float().cpu().numpy().astype(np.float64)
+        lse_h = lse[b, h].cpu().numpy().astype(np.float64)
+        o_ref, lse_ref = attention_reference(q[b, h], k[b, h], v[b, h], w.scale, causal=causal)
+        assert_close(o_h, lse_h, o_ref, lse_ref, w.dtype, f"wide N=8200 b{b} h{h} causal={causal}")
+
+
+def test_naive_refuses_host_workspace():
+    """A workspace on the host would be written through by the kernels: the
+    binding refuses it before any call."""
+    x = torch.zeros((1, 1, 64, 64), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError, match="device"):
+        fa.attn_naive_fwd(x, x, x, workspace=torch.empty(1 << 16, dtype=torch.uint8))
 
 
 @pytest.mark.parametrize("dtype", ["fp32", "fp16", "bf16"])
