@@ -82,30 +82,49 @@ def _counter_rows(path: str, counter: str):
     return sorted(rows)
 
 
+# Kernels each entry point dispatches (name patterns in the profiler's records).
+ENTRY_KERNELS = {"flash": r"flash_fwd_", "naive": r"naive_"}
+
+
+def _short_name(name: str) -> str:
+    return name.replace("void fa::(anonymous namespace)::", "").split("(")[0].replace("fa::", "").replace(" ", "")
+
+
+def launch_counter(path: str, counter: str, entry: str, launches: int, warmup: int):
+    """Per-launch total of one counter over every kernel an entry point
+    dispatches: the dispatches matching ENTRY_KERNELS[entry], in order, fall
+    into warmup + launches equal groups (one per call; a call may dispatch
+    several kernels, e.g. the three passes of the naive path or the two
+    launches of a split grid); the warm-up groups are left out and the rest
+    averaged. Returns (kernel names, dispatches per launch, mean per launch)."""
+    import re
+
+    rows = [r for r in _counter_rows(path, counter) if re.search(ENTRY_KERNELS[entry], r[1])]
+    total = warmup + launches
+    if not rows or len(rows) % total:
+        raise ValueError(f"{path}: {len(rows)} {entry} dispatches do not split into {total} launches")
+    per = len(rows) // total
+    timed = rows[warmup * per:]
+    names = sorted({_short_name(n) for _, n, _, _ in timed})
+    return names, per, sum(v for _, _, _, v in timed) / launches
+
+
 def record_traffic(fetch_csv: str, write_csv: str, copy_fetch_csv: str, copy_write_csv: str,
-                   workload: str = "n32768_d128_bf16", entry: str = "flash",
+                   workload: str = "n32768_d128_bf16", entry: str = "flash", launches: int = 2, warmup: int = 1,
                    copy_bytes: int = 1 << 30) -> dict:
-    """Write the HBM-traffic record of `workload` into profiles/traffic.json.
+    """Write the HBM-traffic record of (entry, workload) into profiles/traffic.json.
 
     Inputs: the counter files of four rocprofv3 --pmc runs: FETCH_SIZE and
-    WRITE_SIZE (KiB per dispatch) of `bench.py --steps 2 --warmup 1
-    --no-cpu-baseline`, and the same two counters for `bench.py
-    --copy-calibration 1073741824`. The kernel is the first one dispatched
-    (the workload's launch); its first dispatch (warm-up) is left out and the
-    rest averaged. Each counter is scaled so that the copy reads and writes
-    exactly `copy_bytes`. The record carries the current kernel source hash,
-    so bench.py uses it only for the binary it was taken on.
+    WRITE_SIZE (KiB per dispatch) of `bench.py --workload W --entry E --steps
+    <launches> --warmup <warmup> --no-cpu-baseline --no-also`, and the same two
+    counters for `bench.py --copy-calibration 1073741824`. Every dispatch of
+    the entry point's kernels counts; warm-up calls are left out and the rest
+    averaged per call. Each counter is scaled so that the copy reads and
+    writes exactly `copy_bytes`. The record carries the current kernel source
+    hash, so bench.py uses it only for the binary it was taken on.
     """
     from io_aware_tiled_06_amd import traffic
     from io_aware_tiled_06_amd.workloads import WORKLOADS
-
-    def kernel_mean(path, counter):
-        rows = _counter_rows(path, counter)
-        name, grid = rows[0][1], rows[0][2]
-        vals = [v for _, n, g, v in rows if n == name and g == grid][1:]
-        if not vals:
-            raise ValueError(f"{path}: no timed dispatch of {name}")
-        return name, sum(vals) / len(vals)
 
     def copy_mean(path, counter):
         vals = [v for _, n, _, v in _counter_rows(path, counter) if "copyBuffer" in n]
@@ -113,21 +132,20 @@ def record_traffic(fetch_csv: str, write_csv: str, copy_fetch_csv: str, copy_wri
             raise ValueError(f"{path}: no copy dispatch")
         return sum(vals) / len(vals)
 
-    name, fetch = kernel_mean(fetch_csv, "FETCH_SIZE")
-    _, write = kernel_mean(write_csv, "WRITE_SIZE")
+    names, per, fetch = launch_counter(fetch_csv, "FETCH_SIZE", entry, launches, warmup)
+    _, _, write = launch_counter(write_csv, "WRITE_SIZE", entry, launches, warmup)
     cf, cw = copy_mean(copy_fetch_csv, "FETCH_SIZE"), copy_mean(copy_write_csv, "WRITE_SIZE")
     fs, ws = copy_bytes / (cf * 1024), copy_bytes / (cw * 1024)
     w = WORKLOADS[workload]
     rd, wr = round(fetch * 1024 * fs), round(write * 1024 * ws)
-    short = name.replace("void fa::(anonymous namespace)::", "").split("(")[0].replace("fa::", "").replace(" ", "")
     try:
         with open(TRAFFIC_FILE) as f:
             data = json.load(f)
     except (OSError, ValueError):
         data = {}
     data[f"{entry}:{workload}"] = {
-        "source_hash": kernel_source_hash(entry), "kernel": short,
-        "fetch_kib_per_dispatch": fetch, "write_kib_per_dispatch": write,
+        "source_hash": kernel_source_hash(entry), "kernels": names, "dispatches_per_launch": per,
+        "fetch_kib_per_launch": fetch, "write_kib_per_launch": write,
         "fetch_scale": round(fs, 6), "write_scale": round(ws, 6),
         "hbm_read_bytes_per_launch": rd, "hbm_write_bytes_per_launch": wr, "hbm_bytes_per_launch": rd + wr,
         "compulsory_bytes": traffic.compulsory_bytes(w.B, w.H, w.N, w.d, w.elem_bytes),
@@ -222,11 +240,12 @@ class ClockSampler:
         return out
 
 
-def time_forward(name: str, steps: int = 20, warmup: int = 5) -> dict:
-    """Kernel time of the fused forward pass on another named workload (HIP
-    events on the launch stream around each launch, the launches queued
-    back to back): the metric names both the 4096- and the 32768-token
-    cases."""
+def time_entry(name: str, entry: str = "flash", steps: int = 20, warmup: int = 5) -> dict:
+    """Kernel time of one entry point (fused or three-pass) on a named
+    workload: HIP events on the launch stream around each call, the calls
+    queued back to back behind a spin kernel. The metric names both the 4096-
+    and the 32768-token cases; the comparison with the three-pass path uses
+    the same timing."""
     import numpy as np
     import torch
 
@@ -239,8 +258,15 @@ def time_forward(name: str, steps: int = 20, warmup: int = 5) -> dict:
     tdt = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}[w.dtype]
     tq, tk, tv = (torch.from_numpy(x).to(tdt).to(dev) for x in make_inputs(w))
     o = torch.empty_like(tq)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    ws = None
+    if entry == "naive":
+        ws = torch.empty(fa.attn_naive_workspace_bytes(w.B, w.H, w.N, w.dtype), dtype=torch.uint8, device=dev)
+        call = lambda: fa.attn_naive_fwd(tq, tk, tv, w.scale, out=o, workspace=ws)  # noqa: E731
+    else:
+        call = lambda: fa.flash_attn_fwd(tq, tk, tv, w.scale, out=o)  # noqa: E731
     for _ in range(warmup):
-        fa.flash_attn_fwd(tq, tk, tv, w.scale, out=o)
+        call()
     stream = torch.cuda.current_stream(dev)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     torch.cuda.synchronize(dev)
@@ -251,14 +277,51 @@ def time_forward(name: str, steps: int = 20, warmup: int = 5) -> dict:
     torch.cuda._sleep(20_000_000)
     for a, b in ev:
         a.record(stream)
-        fa.flash_attn_fwd(tq, tk, tv, w.scale, out=o)
+        call()
         b.record(stream)
     torch.cuda.synchronize(dev)
     ms = [a.elapsed_time(b) for a, b in ev]
     tflops = traffic.attention_flops(w.B, w.H, w.N, w.d) / (float(np.mean(ms)) * 1e-3) / 1e12
-    return {"workload": name, "kernel_ms": round(float(np.mean(ms)), 4),
-            "kernel_ms_median": round(float(np.median(ms)), 4), "tflops": round(tflops, 3),
-            "frac_of_peak": round(tflops / PEAK_TFLOPS[w.dtype], 4), "steps": steps}
+    out = {"workload": name, "entry": entry, "kernel_ms": round(float(np.mean(ms)), 4),
+           "kernel_ms_median": round(float(np.median(ms)), 4), "tflops": round(tflops, 3),
+           "frac_of_peak": round(tflops / PEAK_TFLOPS[w.dtype], 4), "steps": steps,
+           "workspace_bytes": int(ws.numel()) if ws is not None else 0}
+    del ws
+    torch.cuda.empty_cache()
+    return out
+
+
+def time_forward(name: str, steps: int = 20, warmup: int = 5) -> dict:
+    """Kernel time of the fused forward pass on a named workload."""
+    out = time_entry(name, "flash", steps, warmup)
+    for k in ("entry", "workspace_bytes"):
+        out.pop(k)
+    return out
+
+
+COMPARE_WORKLOADS = ("n4096_d128_bf16", "n10000_d128_fp16", "b32_n512_d64_bf16", "n32768_d128_bf16")
+
+
+def compare_paths(steps: int = 20) -> None:
+    """The fused and the three-pass path on each half-precision workload: one
+    JSON line per (workload, path) with kernel time, TFLOP/s, fraction of the
+    matrix-core peak, the three-pass workspace, and the measured HBM bytes
+    per call with M/C (measured over compulsory bytes) when profiles/traffic.json
+    holds a record taken on the current kernel source."""
+    from io_aware_tiled_06_amd import traffic
+    from io_aware_tiled_06_amd.workloads import WORKLOADS
+
+    for name in COMPARE_WORKLOADS:
+        w = WORKLOADS[name]
+        for entry in ("flash", "naive"):
+            n = steps if entry == "flash" or w.N < 32768 else max(3, steps // 5)
+            rec = time_entry(name, entry, n, 2)
+            hbm = measured_traffic(name, entry)
+            c = traffic.compulsory_bytes(w.B, w.H, w.N, w.d, w.elem_bytes)
+            rec["hbm_bytes_per_call"] = hbm
+            rec["m_over_c"] = round(hbm / c, 3) if hbm else None
+            rec["compulsory_bytes"] = c
+            print(json.dumps(rec), flush=True)
 
 
 def cpu_baseline(w, q, k, v, target_s: float = 15.0):
@@ -379,9 +442,9 @@ def traffic_sweep(entry: str) -> None:
 CROSSOVER_N = (16, 32, 64, 128, 256, 512, 1024, 2048, 4096)
 
 
-def crossover_sweep(reps: int = 10) -> None:
-    """Fused versus three-pass path at a fixed amount of work: H = 16, d = 128,
-    bf16, B chosen so that B*H*N^2 = 16*4096^2 at every N. For each N and path:
+def crossover_sweep(reps: int = 10, d: int = 128, dtype: str = "bf16") -> None:
+    """Fused versus three-pass path at a fixed amount of work: H = 16, head
+    size d, element type dtype, B chosen so that B*H*N^2 = 16*4096^2 at every N. For each N and path:
     median kernel time over `reps` launches (HIP events on the current stream,
     after 2 warm-ups) and the device memory the call needs beyond Q, K, V
     (the outputs, plus the three-pass workspace), from torch's allocator peak.
@@ -398,12 +461,13 @@ def crossover_sweep(reps: int = 10) -> None:
         __graft_entry__.build()
     dev = torch.device("cuda:0")
     gen = torch.Generator(device=dev).manual_seed(6)
+    tdt = {"bf16": torch.bfloat16, "fp16": torch.float16}[dtype]
     work = 16 * 4096 * 4096
     faster_naive = []
     for n in CROSSOVER_N:
         b = max(1, work // (16 * n * n))
-        shape = (b, 16, n, 128)
-        q, k, v = (torch.randn(shape, generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        shape = (b, 16, n, d)
+        q, k, v = (torch.randn(shape, generator=gen, device=dev, dtype=torch.float32).to(tdt)
                    for _ in range(3))
         ms = {}
         for entry in ("flash", "naive"):
@@ -414,7 +478,7 @@ def crossover_sweep(reps: int = 10) -> None:
             lse = torch.empty((b, 16, n), dtype=torch.float32, device=dev)
             ws = None
             if entry == "naive":
-                ws = torch.empty(fa.attn_naive_workspace_bytes(b, 16, n, "bf16"), dtype=torch.uint8, device=dev)
+                ws = torch.empty(fa.attn_naive_workspace_bytes(b, 16, n, dtype), dtype=torch.uint8, device=dev)
             call = (lambda: fa.attn_naive_fwd(q, k, v, out=o, workspace=ws)) if entry == "naive" else \
                 (lambda: fa.flash_attn_fwd(q, k, v, out=o))
             for _ in range(2):
@@ -429,9 +493,9 @@ def crossover_sweep(reps: int = 10) -> None:
             t = float(np.median([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]))
             extra = torch.cuda.max_memory_allocated(dev) - base
             ms[entry] = t
-            print(json.dumps({"crossover": entry, "N": n, "B": b, "H": 16, "d": 128, "dtype": "bf16",
+            print(json.dumps({"crossover": entry, "N": n, "B": b, "H": 16, "d": d, "dtype": dtype,
                               "kernel_ms": round(t, 5),
-                              "tflops": round(4.0 * b * 16 * n * n * 128 / (t * 1e-3) / 1e12, 2),
+                              "tflops": round(4.0 * b * 16 * n * n * d / (t * 1e-3) / 1e12, 2),
                               "extra_device_bytes": int(extra)}), flush=True)
             del o, lse, ws
             torch.cuda.empty_cache()
@@ -439,8 +503,50 @@ def crossover_sweep(reps: int = 10) -> None:
             faster_naive.append(n)
         del q, k, v
         torch.cuda.empty_cache()
-    print(json.dumps({"crossover_naive_faster_up_to_N": max(faster_naive) if faster_naive else None,
+    print(json.dumps({"d": d, "dtype": dtype,
+                      "crossover_naive_faster_up_to_N": max(faster_naive) if faster_naive else None,
                       "naive_faster_at": faster_naive}), flush=True)
+
+
+def collect_counters(out_dir: str, workloads, entries, copy_bytes: int = 1 << 30) -> None:
+    """Measure HBM bytes per call of each (entry, workload) and write the
+    records into profiles/traffic.json.
+
+    Runs, each as a child process under `rocprofv3 --pmc <counter> -f csv`
+    (one counter per pass; this process itself never touches the GPU):
+      bench.py --copy-calibration <copy_bytes>                  FETCH_SIZE, WRITE_SIZE
+      bench.py --workload W --entry E --steps 2 --warmup 1
+               --no-cpu-baseline --no-also                       FETCH_SIZE, WRITE_SIZE
+    into out_dir/<name>/run_counter_collection.csv, then record_traffic on the
+    four files of each pair. A pass that fails or outlives its time limit
+    stops the collection."""
+    import subprocess
+
+    me = os.path.abspath(__file__)
+
+    def pmc(name, counter, args, limit=300):
+        d = os.path.join(out_dir, f"{name}_{counter}")
+        cmd = ["timeout", "-s", "KILL", str(limit), "rocprofv3", "--pmc", counter, "-f", "csv", "-d", d, "-o", "run",
+               "--", sys.executable, me, *args]
+        print(f"[counters] {name} {counter}", file=sys.stderr, flush=True)
+        with open(os.path.join(out_dir, f"{name}_{counter}.log"), "w") as log:
+            r = subprocess.run(cmd, stdout=log, stderr=subprocess.STDOUT)
+        csv_path = os.path.join(d, "run_counter_collection.csv")
+        if r.returncode != 0 or not os.path.exists(csv_path):
+            raise RuntimeError(f"{' '.join(cmd)} failed (status {r.returncode})")
+        return csv_path
+
+    os.makedirs(out_dir, exist_ok=True)
+    copy = {c: pmc("copy", c, ["--copy-calibration", str(copy_bytes)]) for c in ("FETCH_SIZE", "WRITE_SIZE")}
+    for wl in workloads:
+        for entry in entries:
+            args = ["--workload", wl, "--entry", entry, "--steps", "2", "--warmup", "1", "--no-cpu-baseline",
+                    "--no-also"]
+            f = pmc(f"{entry}_{wl}", "FETCH_SIZE", args)
+            w = pmc(f"{entry}_{wl}", "WRITE_SIZE", args)
+            rec = record_traffic(f, w, copy["FETCH_SIZE"], copy["WRITE_SIZE"], workload=wl, entry=entry,
+                                 launches=2, warmup=1, copy_bytes=copy_bytes)
+            print(json.dumps({"counters": f"{entry}:{wl}", **rec}), flush=True)
 
 
 def bwd_compulsory_bytes(w) -> int:
@@ -454,8 +560,10 @@ def bwd_compulsory_bytes(w) -> int:
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200,
+                    help="timed calls (with --record-traffic: the timed calls of the profiled run)")
+    ap.add_argument("--warmup", type=int, default=10,
+                    help="untimed calls first (with --record-traffic: those of the profiled run)")
     ap.add_argument("--workload", default="n32768_d128_bf16")
     ap.add_argument("--entry", choices=["flash", "naive"], default="flash")
     ap.add_argument("--backward", action="store_true",
@@ -472,9 +580,24 @@ def main() -> int:
                     help="write profiles/traffic.json from four rocprofv3 --pmc counter files and exit (no GPU)")
     ap.add_argument("--crossover-sweep", action="store_true",
                     help="only run the fused-versus-three-pass sweep at fixed work (time and memory) and exit")
+    ap.add_argument("--crossover-d", type=int, default=128, choices=[64, 128],
+                    help="head size of the crossover sweep")
+    ap.add_argument("--compare-paths", action="store_true",
+                    help="only time the fused and the three-pass path on the four half-precision workloads and exit")
+    ap.add_argument("--collect-counters", metavar="OUT_DIR", default=None,
+                    help="only run the rocprofv3 FETCH_SIZE/WRITE_SIZE passes (child processes) of --workloads x "
+                         "--entries and write profiles/traffic.json, then exit")
+    ap.add_argument("--workloads", default="n32768_d128_bf16", help="comma list for --collect-counters")
+    ap.add_argument("--entries", default="flash", help="comma list for --collect-counters")
+    ap.add_argument("--no-also", action="store_true",
+                    help="skip the extra 4096-token timing of the default workload (counter collection)")
     args = ap.parse_args()
     if args.record_traffic:
-        print(json.dumps(record_traffic(*args.record_traffic, workload=args.workload)), flush=True)
+        print(json.dumps(record_traffic(*args.record_traffic, workload=args.workload, entry=args.entry,
+                                        launches=args.steps, warmup=args.warmup)), flush=True)
+        return 0
+    if args.collect_counters:
+        collect_counters(args.collect_counters, args.workloads.split(","), args.entries.split(","))
         return 0
     if args.copy_calibration:
         copy_calibration(args.copy_calibration, 3)
@@ -483,7 +606,10 @@ def main() -> int:
         traffic_sweep(args.traffic_sweep)
         return 0
     if args.crossover_sweep:
-        crossover_sweep()
+        crossover_sweep(d=args.crossover_d)
+        return 0
+    if args.compare_paths:
+        compare_paths()
         return 0
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the library has no multi-GPU path",
@@ -599,7 +725,8 @@ def main() -> int:
         line["clock"] = clock
     if args.backward:
         line["roofline"]["kernels"] = "bwd_delta + bwd_dq + bwd_dkdv (one backward pass)"
-    if args.entry == "flash" and not (args.causal or args.backward) and w.name == "n32768_d128_bf16":
+    if (args.entry == "flash" and not (args.causal or args.backward or args.no_also)
+            and w.name == "n32768_d128_bf16"):
         print("[bench] the 4096-token forward (the metric's other case)", file=sys.stderr, flush=True)
         line["also"] = time_forward("n4096_d128_bf16")
     if not args.no_cpu_baseline and not args.backward:

@@ -58,8 +58,11 @@ HEADER = ('"Correlation_Id","Dispatch_Id","Agent_Id","Queue_Id","Process_Id","Th
           '"Kernel_Id","Kernel_Name","Workgroup_Size","LDS_Block_Size","Scratch_Size","VGPR_Count",'
           '"Accum_VGPR_Count","SGPR_Count","Counter_Name","Counter_Value","Start_Timestamp","End_Timestamp"\n')
 KERN = "void fa::(anonymous namespace)::flash_fwd_half<fa::BF16, 128, 8, 1, false, false>(fa::FwdParams)"
-OTHER = "void fa::(anonymous namespace)::flash_fwd_half<fa::BF16, 128, 4, 2, false, false>(fa::FwdParams)"
+TORCH = "void at::native::elementwise_kernel<128, 4>(int, float)"
 COPY = "__amd_rocclr_copyBuffer"
+NAIVE = ["void fa::(anonymous namespace)::naive_scores_half<fa::BF16, 128>(fa::NaiveParams)",
+         "void fa::(anonymous namespace)::naive_softmax<fa::BF16>(fa::NaiveParams)",
+         "void fa::(anonymous namespace)::naive_pv_half<fa::BF16, 128>(fa::NaiveParams)"]
 
 
 def _csv(path, counter, rows):
@@ -70,21 +73,51 @@ def _csv(path, counter, rows):
     return str(path)
 
 
-def test_record_traffic(tmp_path, monkeypatch):
-    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "traffic.json"))
-    # warm-up dispatch (left out), two timed ones, then another kernel (ignored)
-    f = _csv(tmp_path / "f.csv", "FETCH_SIZE", [(KERN, 1048576, 999.0), (KERN, 1048576, 100.0),
-                                                 (KERN, 1048576, 300.0), (OTHER, 131072, 7.0)])
-    w = _csv(tmp_path / "w.csv", "WRITE_SIZE", [(KERN, 1048576, 5.0), (KERN, 1048576, 50.0),
-                                                 (KERN, 1048576, 70.0), (OTHER, 131072, 7.0)])
+def _copies(tmp_path):
     cf = _csv(tmp_path / "cf.csv", "FETCH_SIZE", [("elementwise", 1, 1.0), (COPY, 1, 512.0), (COPY, 1, 512.0)])
     cw = _csv(tmp_path / "cw.csv", "WRITE_SIZE", [(COPY, 1, 1024.0), (COPY, 1, 1024.0)])
+    return cf, cw
+
+
+def test_record_traffic(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "traffic.json"))
+    # a torch kernel (ignored), the warm-up call (left out), two timed calls
+    f = _csv(tmp_path / "f.csv", "FETCH_SIZE", [(TORCH, 64, 7.0), (KERN, 1048576, 999.0), (KERN, 1048576, 100.0),
+                                                 (KERN, 1048576, 300.0)])
+    w = _csv(tmp_path / "w.csv", "WRITE_SIZE", [(TORCH, 64, 7.0), (KERN, 1048576, 5.0), (KERN, 1048576, 50.0),
+                                                 (KERN, 1048576, 70.0)])
+    cf, cw = _copies(tmp_path)
     rec = bench.record_traffic(f, w, cf, cw, copy_bytes=1 << 20)
     # copy of 1 MiB read as 512 KiB -> fetch scale 2; written as 1024 KiB -> scale 1
     assert rec["fetch_scale"] == 2.0 and rec["write_scale"] == 1.0
-    assert rec["fetch_kib_per_dispatch"] == 200.0 and rec["write_kib_per_dispatch"] == 60.0
+    assert rec["fetch_kib_per_launch"] == 200.0 and rec["write_kib_per_launch"] == 60.0
     assert rec["hbm_read_bytes_per_launch"] == 200 * 1024 * 2
     assert rec["hbm_write_bytes_per_launch"] == 60 * 1024
-    assert rec["kernel"] == "flash_fwd_half<BF16,128,8,1,false,false>"
+    assert rec["kernels"] == ["flash_fwd_half<BF16,128,8,1,false,false>"] and rec["dispatches_per_launch"] == 1
     assert rec["source_hash"] == bench.kernel_source_hash("flash")
     assert bench.measured_traffic("n32768_d128_bf16", "flash") == rec["hbm_bytes_per_launch"]
+
+
+def test_record_traffic_sums_every_kernel_of_a_call(tmp_path, monkeypatch):
+    """The three-pass path dispatches three kernels per call: the record sums
+    all of them per call, after the warm-up call."""
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "traffic.json"))
+    vals = [[1000.0, 1000.0, 1000.0], [10.0, 20.0, 30.0], [30.0, 20.0, 10.0]]  # warm-up, then two calls
+    f = _csv(tmp_path / "f.csv", "FETCH_SIZE", [(NAIVE[i], 8, v) for call in vals for i, v in enumerate(call)])
+    w = _csv(tmp_path / "w.csv", "WRITE_SIZE", [(NAIVE[i], 8, 2 * v) for call in vals for i, v in enumerate(call)])
+    cf, cw = _copies(tmp_path)
+    rec = bench.record_traffic(f, w, cf, cw, workload="b32_n512_d64_bf16", entry="naive", copy_bytes=1 << 20)
+    assert rec["dispatches_per_launch"] == 3 and len(rec["kernels"]) == 3
+    assert rec["fetch_kib_per_launch"] == 60.0 and rec["write_kib_per_launch"] == 120.0
+    assert rec["source_hash"] == bench.kernel_source_hash("naive")
+    assert bench.measured_traffic("b32_n512_d64_bf16", "naive") == rec["hbm_bytes_per_launch"]
+
+
+def test_record_traffic_rejects_uneven_dispatches(tmp_path, monkeypatch):
+    import pytest
+
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "traffic.json"))
+    f = _csv(tmp_path / "f.csv", "FETCH_SIZE", [(KERN, 1, 1.0)] * 4)
+    cf, cw = _copies(tmp_path)
+    with pytest.raises(ValueError):
+        bench.record_traffic(f, f, cf, cw, copy_bytes=1 << 20)  # 4 dispatches are not 3 calls
