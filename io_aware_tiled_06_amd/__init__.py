@@ -22,6 +22,8 @@ __all__ = [
     "attn_naive_workspace_bytes",
     "lib",
     "LIB_PATH",
+    "POISON_LIB_PATH",
+    "using_library",
     "EXPORTED_SYMBOLS",
     "DTYPE_CODE",
     "FA_OK",
@@ -38,6 +40,9 @@ __all__ = [
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libflashattn.so")
+# The race-guard build of the same sources (every LDS slot a copy refills
+# holds NaN until the copy lands); see using_library().
+POISON_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libflashattn_poison.so")
 EXPORTED_SYMBOLS = ("flash_attn_fwd", "flash_attn_fwd_causal", "flash_attn_bwd", "flash_attn_bwd_causal",
                     "flash_attn_bwd_noalloc", "attn_naive_workspace_bytes", "attn_naive_fwd", "fa_strerror")
 
@@ -62,32 +67,61 @@ class FlashAttnError(RuntimeError):
 
 
 def lib() -> ctypes.CDLL:
-    """The loaded libflashattn.so with argument types declared."""
+    """The loaded libflashattn.so (or the library selected by using_library)
+    with argument types declared."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError(
-                f"{LIB_PATH} is not built; run `python -m io_aware_tiled_06_amd.build` (needs hipcc)")
-        L = ctypes.CDLL(LIB_PATH)
-        vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
-        L.flash_attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
-        L.flash_attn_fwd.restype = i
-        L.flash_attn_fwd_causal.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
-        L.flash_attn_fwd_causal.restype = i
-        for name in ("flash_attn_bwd", "flash_attn_bwd_causal"):
-            fn = getattr(L, name)
-            fn.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
-            fn.restype = i
-        L.flash_attn_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
-        L.flash_attn_bwd_noalloc.restype = i
-        L.attn_naive_workspace_bytes.argtypes = [i, i, i, i]
-        L.attn_naive_workspace_bytes.restype = sz
-        L.attn_naive_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, sz, vp]
-        L.attn_naive_fwd.restype = i
-        L.fa_strerror.argtypes = [i]
-        L.fa_strerror.restype = ctypes.c_char_p
-        _lib = L
+        _lib = _load(LIB_PATH)
     return _lib
+
+
+_loaded = {}
+
+
+def using_library(path: str):
+    """Context manager: every call of this module inside the block goes to the
+    library at `path` (a build of the same sources, e.g. POISON_LIB_PATH),
+    then back to the one before. Not thread-safe; meant for tests."""
+    import contextlib
+
+    @contextlib.contextmanager
+    def _ctx():
+        global _lib
+        prev = _lib
+        _lib = _load(path)
+        try:
+            yield _lib
+        finally:
+            _lib = prev
+
+    return _ctx()
+
+
+def _load(path: str) -> ctypes.CDLL:
+    if path in _loaded:
+        return _loaded[path]
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run `python -m io_aware_tiled_06_amd.build all` (needs hipcc)")
+    L = ctypes.CDLL(path)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    L.flash_attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
+    L.flash_attn_fwd.restype = i
+    L.flash_attn_fwd_causal.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
+    L.flash_attn_fwd_causal.restype = i
+    for name in ("flash_attn_bwd", "flash_attn_bwd_causal"):
+        fn = getattr(L, name)
+        fn.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
+        fn.restype = i
+    L.flash_attn_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
+    L.flash_attn_bwd_noalloc.restype = i
+    L.attn_naive_workspace_bytes.argtypes = [i, i, i, i]
+    L.attn_naive_workspace_bytes.restype = sz
+    L.attn_naive_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, sz, vp]
+    L.attn_naive_fwd.restype = i
+    L.fa_strerror.argtypes = [i]
+    L.fa_strerror.restype = ctypes.c_char_p
+    _loaded[path] = L
+    return L
 
 
 def strerror(status: int) -> str:

@@ -1,6 +1,8 @@
 """Build libflashattn.so (gfx950) in-tree with hipcc.
 
-    python -m io_aware_tiled_06_amd.build
+    python -m io_aware_tiled_06_amd.build            # libflashattn.so
+    python -m io_aware_tiled_06_amd.build poison     # libflashattn_poison.so (race guard)
+    python -m io_aware_tiled_06_amd.build all        # both
 
 Every source is compiled for gfx950 only. The per-kernel register, LDS and
 scratch usage reported by the compiler is written next to the objects
@@ -23,6 +25,10 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB_NAME = "libflashattn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
+# Race-guard variant of the same sources (FA_DEBUG_POISON): every LDS slot a
+# copy refills holds NaN until the copy lands. For tests only; slower.
+POISON_LIB_PATH = os.path.join(PKG, "libflashattn_poison.so")
+VARIANTS = {None: (LIB_PATH, []), "poison": (POISON_LIB_PATH, ["-DFA_DEBUG_POISON"])}
 SOURCES = ["api.hip", "flash_fwd.hip", "flash_bwd.hip", "naive.hip"]
 ARCH = "gfx950"
 
@@ -56,9 +62,12 @@ def _hipcc() -> str:
     return exe
 
 
-def _compile(src: str) -> tuple[str, str]:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [_hipcc(), *HIPCC_FLAGS, *SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, variant=None) -> tuple[str, str]:
+    objdir = BUILD if variant is None else os.path.join(BUILD, variant)
+    os.makedirs(objdir, exist_ok=True)
+    obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
+    cmd = [_hipcc(), *HIPCC_FLAGS, *SOURCE_FLAGS.get(src, []), *VARIANTS[variant][1], "-c", os.path.join(CSRC, src),
+           "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
@@ -88,35 +97,48 @@ def _check_spills(kernels: dict) -> None:
         raise RuntimeError(f"kernels use scratch memory (register spills): {sorted(bad)}")
 
 
-def build(verbose: bool = False) -> str:
-    """Compile all sources and link the shared library; returns its path."""
+def build(verbose: bool = False, variant=None) -> str:
+    """Compile all sources and link the shared library (variant None) or the
+    race-guard library (variant "poison"); returns its path."""
     os.makedirs(BUILD, exist_ok=True)
+    lib_path = VARIANTS[variant][0]
     with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        results = list(ex.map(_compile, SOURCES))
+        results = list(ex.map(lambda src: _compile(src, variant), SOURCES))
     objs = [o for o, _ in results]
     report = "\n".join(r for _, r in results)
-    with open(os.path.join(BUILD, "resource_usage.txt"), "w") as f:
+    tag = "" if variant is None else f"_{variant}"
+    with open(os.path.join(BUILD, f"resource_usage{tag}.txt"), "w") as f:
         f.write(report)
     kernels = parse_resource_usage(report)
     if not kernels:
         raise RuntimeError("no kernel-resource-usage remarks found in the compiler output")
-    _check_spills(kernels)
-    with open(os.path.join(BUILD, "resource_summary.txt"), "w") as f:
+    if variant is None:
+        _check_spills(kernels)  # the race-guard build may spill (its extra stores); it is for tests only
+    with open(os.path.join(BUILD, f"resource_summary{tag}.txt"), "w") as f:
         for name, v in sorted(kernels.items()):
             f.write(f"{name} VGPRs={v.get('VGPRs')} AGPRs={v.get('AGPRs')} "
                     f"scratch={v.get('ScratchSize [bytes/lane]')} occupancy={v.get('Occupancy [waves/SIMD]')} "
                     f"LDS={v.get('LDS Size [bytes/block]')}\n")
-    tmp = LIB_PATH + ".tmp"
+    tmp = lib_path + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, lib_path)
     if verbose:
-        print(f"built {LIB_PATH}")
-    return LIB_PATH
+        print(f"built {lib_path}")
+    return lib_path
+
+
+def build_all(verbose: bool = False) -> None:
+    """The library and its race-guard variant."""
+    build(verbose)
+    build(verbose, "poison")
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    if len(sys.argv) > 1 and sys.argv[1] == "all":
+        build_all(verbose=True)
+    else:
+        build(verbose=True, variant=sys.argv[1] if len(sys.argv) > 1 else None)
     sys.exit(0)

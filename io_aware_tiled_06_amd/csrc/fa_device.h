@@ -146,7 +146,45 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // later transposing LDS read (it cannot tell them apart from the copy's
 // destination). Every LDS read of copied data is ordered by hand instead: an
 // explicit vmcnt wait (vm_wait) and a workgroup barrier, never by the compiler.
+// Race-guard build (FA_DEBUG_POISON): before a copy is issued, this lane's
+// destination bytes are filled with all-ones (a NaN in fp32, fp16 and bf16)
+// and the write is waited for. A slot then holds NaN from the moment it is
+// refilled -- after the barrier that follows its last read -- until the new
+// tile lands, so a read that is not ordered after the copy's wait and
+// barrier, or a copy issued into a slot still being read, shows up as NaN in
+// the outputs instead of as stale or early data.
+#ifdef FA_DEBUG_POISON
+// One temporary register, written and consumed inside the block; the stores
+// have completed (lgkmcnt(0)) before the block ends.
+__device__ __forceinline__ void poison_lds(uint32_t lds, int bytes_per_lane) {
+  const uint32_t a = lds + (uint32_t)(threadIdx.x & 63) * (uint32_t)bytes_per_lane;
+  uint32_t tmp;
+  if (bytes_per_lane == 16)
+    asm volatile(
+        "v_mov_b32 %0, -1\n\t"
+        "ds_write_b32 %1, %0\n\t"
+        "ds_write_b32 %1, %0 offset:4\n\t"
+        "ds_write_b32 %1, %0 offset:8\n\t"
+        "ds_write_b32 %1, %0 offset:12\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(tmp)
+        : "v"(a)
+        : "memory");
+  else
+    asm volatile(
+        "v_mov_b32 %0, -1\n\t"
+        "ds_write_b32 %1, %0\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(tmp)
+        : "v"(a)
+        : "memory");
+}
+#endif
+
 __device__ __forceinline__ void load_lds16(i32x4 rsrc, uint32_t lds, uint32_t voff) {
+#ifdef FA_DEBUG_POISON
+  poison_lds(lds, 16);
+#endif
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
@@ -162,6 +200,9 @@ __device__ __forceinline__ void load_lds16(i32x4 rsrc, uint32_t lds, uint32_t vo
 // The same with 4 bytes per lane (buffer_load_dword ... lds): lane i fills
 // LDS bytes [lds + 4 i, lds + 4 i + 4).
 __device__ __forceinline__ void load_lds4(i32x4 rsrc, uint32_t lds, uint32_t voff) {
+#ifdef FA_DEBUG_POISON
+  poison_lds(lds, 4);
+#endif
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"

@@ -50,6 +50,18 @@ def test_library_exports_every_declared_symbol(L):
         assert re.search(rf"\bT {name}$", out, re.M), name
 
 
+def test_race_guard_library_exports_every_declared_symbol(L):
+    """The race-guard build (FA_DEBUG_POISON) of the same sources loads and
+    exports the same interface."""
+    if not os.path.exists(fa.POISON_LIB_PATH):
+        import __graft_entry__
+
+        __graft_entry__.build()
+    P_ = ctypes.CDLL(fa.POISON_LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(P_, name), name
+
+
 def test_strerror(L):
     for st in range(8):
         assert isinstance(fa.strerror(st), str) and fa.strerror(st)
