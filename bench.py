@@ -15,7 +15,10 @@ drawn with sigma 3). Prints one JSON line:
              `traffic` is the measured HBM bytes per launch from the committed
              rocprofv3 counter summary when it matches the current kernel source
   cpu_baseline  the float64 CPU oracle timed on this host on a bounded sample of
-             the same workload (whole query rows, about 15 s of work)
+             the same workload (whole query rows, about 10 s of work)
+
+The default 1000 timed calls keep the GPU busy for about 8 s at 32K, long
+enough for a utilisation sampler running beside the benchmark to see it.
   also       (default workload only) the kernel time and TFLOP/s of the
              4096-token case (B=1, H=8, d=128, bf16), the metric's other size
 """
@@ -324,7 +327,7 @@ def compare_paths(steps: int = 20) -> None:
             print(json.dumps(rec), flush=True)
 
 
-def cpu_baseline(w, q, k, v, target_s: float = 15.0):
+def cpu_baseline(w, q, k, v, target_s: float = 10.0):
     """Time the float64 oracle for about target_s seconds on whole query rows of
     the workload (head by head)."""
     import numpy as np
@@ -560,9 +563,9 @@ def bwd_compulsory_bytes(w) -> int:
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200,
+    ap.add_argument("--steps", type=int, default=1000,
                     help="timed calls (with --record-traffic: the timed calls of the profiled run)")
-    ap.add_argument("--warmup", type=int, default=10,
+    ap.add_argument("--warmup", type=int, default=20,
                     help="untimed calls first (with --record-traffic: those of the profiled run)")
     ap.add_argument("--workload", default="n32768_d128_bf16")
     ap.add_argument("--entry", choices=["flash", "naive"], default="flash")
