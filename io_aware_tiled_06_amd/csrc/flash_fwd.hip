@@ -804,7 +804,31 @@ hipError_t run_half(const AttnArgs& a) {
   else
     hipLaunchKernelGGL((flash_fwd_half<E, D, kWavesHalf, 1, false, CAUSAL>), dim3(n_main), dim3(kWavesHalf * 64), 0,
                        a.stream, p);
-  if (n_main < full + rest) launch_split(full, rest);
+  if (n_main < full + rest) {
+    // The remaining 128-row tiles as twice as many 64-row tiles, each with its
+    // keys split over two groups of two waves: one workgroup per CU (its LDS),
+    // spread over up to twice the CUs. Blocks run head-major in both tilings,
+    // so the remainder starts at the same (head, first row) in 64-row units.
+    constexpr int kNarrow = 2;
+    const int nq64 = (a.N + kNarrow * 32 - 1) / (kNarrow * 32);
+    const int bh0 = full / p.n_qtiles, qt0 = full % p.n_qtiles;
+    const int blk0 = bh0 * nq64 + qt0 * (BR / (kNarrow * 32));
+    const int n64 = a.B * a.H * nq64 - blk0;
+    if (n64 <= cus) {
+      FwdParams q = p;
+      q.n_qtiles = nq64;
+      q.blk0 = blk0;
+      q.n_blocks = n64;
+      if (a.scale < 0.f)
+        hipLaunchKernelGGL((flash_fwd_half<E, D, kNarrow, 2, true, CAUSAL>), dim3(n64), dim3(kNarrow * 64 * 2), 0,
+                           a.stream, q);
+      else
+        hipLaunchKernelGGL((flash_fwd_half<E, D, kNarrow, 2, false, CAUSAL>), dim3(n64), dim3(kNarrow * 64 * 2), 0,
+                           a.stream, q);
+      return hipGetLastError();
+    }
+    launch_split(full, rest);
+  }
   return hipGetLastError();
 }
 
