@@ -172,7 +172,7 @@ __device__ __forceinline__ bool update_max(float m_tile, float& m_run, float& l_
 // the running maximum uses) and writes the result.
 // ---------------------------------------------------------------------------
 template <class E, int D, int NW, int SPLIT, bool NEG, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64 * SPLIT) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(NW * 64 * SPLIT) __attribute__((amdgpu_waves_per_eu(D == 64 && SPLIT == 1 ? 3 : 2)))
 void flash_fwd_half(FwdParams p) {
   static_assert(SPLIT == 1 || SPLIT == 2, "one or two key groups");
   constexpr int BR = NW * 32;
@@ -345,8 +345,10 @@ void flash_fwd_half(FwdParams p) {
   // the B operand of O^T += V^T P^T (register r is key slot r % 8 of half
   // r / 8). Returns their float32 sum (before rounding: the row normaliser and
   // LSE are float32). Hidden keys get an explicit zero (with c == 0 a hidden
-  // score would give 0 * inf).
-  auto probs = [&](const f32x16& s, u32x4(&pf)[2], int key0, bool mask) {
+  // score would give 0 * inf). MASK_RT: the mask is decided at run time by
+  // `mask`; otherwise no key of the tile is hidden.
+  auto probs = [&](const f32x16& s, u32x4(&pf)[2], int key0, bool mask, auto mask_rt) {
+    constexpr bool MASK_RT = decltype(mask_rt)::value;
     float ls[2];
     const float neg_m = -m_run;
 #pragma unroll
@@ -356,7 +358,7 @@ void flash_fwd_half(FwdParams p) {
         const int r = h * 8 + 2 * w;
         float p0 = exp2_fast(fmaf(s[r], c, neg_m));
         float p1 = exp2_fast(fmaf(s[r + 1], c, neg_m));
-        if (mask) {
+        if (MASK_RT && mask) {
           if (key0 + score_key(0, r, g) > key_lim) p0 = 0.f;
           if (key0 + score_key(0, r + 1, g) > key_lim) p1 = 0.f;
         }
@@ -403,8 +405,8 @@ void flash_fwd_half(FwdParams p) {
     return row_max_scaled_fixed<NEG>(one, c);
   };
   // Tile t's probabilities into pf and its share of the running sum.
-  auto softmax_tile = [&](f32x16& s, u32x4(&pf)[2], int key0, bool mask) {
-    float lt = probs(s, pf, key0, mask);
+  auto softmax_tile = [&](f32x16& s, u32x4(&pf)[2], int key0, bool mask, auto mask_rt) {
+    float lt = probs(s, pf, key0, mask, mask_rt);
     if (__any(!(lt <= kSumLimit))) {
       const float m_new = fmaxf(m_run, tile_max(s, key0, mask));
       if constexpr (kRoundedSum) {
@@ -422,7 +424,7 @@ void flash_fwd_half(FwdParams p) {
         l_run *= alpha;
         m_run = m_new;
       }
-      lt = probs(s, pf, key0, mask);
+      lt = probs(s, pf, key0, mask, mask_rt);
     }
     l_run += lt;
     if constexpr (kRoundedSum) {
@@ -463,8 +465,10 @@ void flash_fwd_half(FwdParams p) {
   // of them. Otherwise everything is decided at run time; the workgroup-wide
   // decisions (copies, barrier) and this wave's own (does it still work on
   // tile t, t+1) are kept apart, so every wave passes the same barriers.
+  // MASK_RT: tile t may need the mask (decided at run time); without it the
+  // step has no masking code at all.
   auto step = [&](int t, f32x16& s_cur, f32x16& s_nxt, const u32x4(&p_prev)[2], u32x4(&p_cur)[2], auto slot_tag,
-                  auto steady_tag) {
+                  auto steady_tag, auto mask_rt) {
     constexpr bool STEADY = decltype(steady_tag)::value;
     const int b = STEADY ? decltype(slot_tag)::value : t % NBUF;
     using Full = std::integral_constant<bool, STEADY>;
@@ -474,7 +478,7 @@ void flash_fwd_half(FwdParams p) {
     if (STEADY || (t >= 1 && t - 1 <= last)) accumulate(vbuf((b + 3) % NBUF), p_prev);
     prefetch_k(kbuf((b + 2) % NBUF));  // stale (unused) past the last tile
     prefetch_v(vbuf(b));               // V_t, landed before this step began
-    if (STEADY || t <= last) softmax_tile(s_cur, p_cur, (kt0 + t) * BC, !STEADY && needs_mask(t));
+    if (STEADY || t <= last) softmax_tile(s_cur, p_cur, (kt0 + t) * BC, !STEADY && needs_mask(t), mask_rt);
     if (STEADY)
       vm_wait<2 * kPer>();
     else
@@ -488,7 +492,7 @@ void flash_fwd_half(FwdParams p) {
     pb[1][0] = pb[0][0];
     pb[1][1] = pb[0][1];
   };
-  step(0, sb[0], sb[1], pb[1], pb[0], std::integral_constant<int, 0>{}, F{});
+  step(0, sb[0], sb[1], pb[1], pb[0], std::integral_constant<int, 0>{}, F{}, T{});
   rotate();
   int t = 1;
   // Steady groups of four steps from t = 1 (mod 4): in every group, copies up
@@ -499,7 +503,7 @@ void flash_fwd_half(FwdParams p) {
       (CAUSAL ? min(n_full, qt * (BR / BC)) : n_full) - (SPLIT == 2 ? half : 0);
 #define FA_STEADY_STEP(I)                                                                      \
   step(t + (I), sb[(I) % 2], sb[((I) + 1) % 2], pb[((I) + 1) % 2], pb[(I) % 2],               \
-       std::integral_constant<int, ((I) + 1) % NBUF>{}, T{})
+       std::integral_constant<int, ((I) + 1) % NBUF>{}, T{}, F{})
   for (; t + 7 < full_all && t + 4 < steady_end; t += 4) {
     FA_STEADY_STEP(0);
     FA_STEADY_STEP(1);
@@ -507,14 +511,22 @@ void flash_fwd_half(FwdParams p) {
     FA_STEADY_STEP(3);
   }
 #undef FA_STEADY_STEP
-  // remaining steps in pairs with the buffers' roles swapped (no register
-  // moves), then at most one more
+  // Remaining steps in pairs with the buffers' roles swapped (no register
+  // moves), then at most one more. Only the ragged last tile and (causal) a
+  // wave's diagonal tile need the mask, so the pairs before the first such
+  // tile of this wave run without masking code (a run-time mask flag costs a
+  // comparison per score). Each wave still runs `steps` steps in all.
+  const int t_mask = min(n_full, CAUSAL ? diag : n_full) - kt0;
+  for (; t + 1 < steps && t + 1 < t_mask; t += 2) {
+    step(t, sb[0], sb[1], pb[1], pb[0], std::integral_constant<int, 0>{}, F{}, F{});
+    step(t + 1, sb[1], sb[0], pb[0], pb[1], std::integral_constant<int, 0>{}, F{}, F{});
+  }
   for (; t + 1 < steps; t += 2) {
-    step(t, sb[0], sb[1], pb[1], pb[0], std::integral_constant<int, 0>{}, F{});
-    step(t + 1, sb[1], sb[0], pb[0], pb[1], std::integral_constant<int, 0>{}, F{});
+    step(t, sb[0], sb[1], pb[1], pb[0], std::integral_constant<int, 0>{}, F{}, T{});
+    step(t + 1, sb[1], sb[0], pb[0], pb[1], std::integral_constant<int, 0>{}, F{}, T{});
   }
   if (t < steps) {
-    step(t, sb[0], sb[1], pb[1], pb[0], std::integral_constant<int, 0>{}, F{});
+    step(t, sb[0], sb[1], pb[1], pb[0], std::integral_constant<int, 0>{}, F{}, T{});
     rotate();
   }
   // P V of this wave's last tile if no step followed it (its V landed before
