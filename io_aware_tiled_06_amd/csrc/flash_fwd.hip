@@ -574,7 +574,47 @@ void flash_fwd_half(FwdParams p) {
   // LSE = ln(2^m * l) = (m + log2 l) * ln 2.
   const float l_tot = pair_sum(l_run);
   const float inv = 1.f / (kRoundedSum ? lr_run : l_tot);
-  if (q_row < N) {
+  // O leaves through LDS where the rings have room: a lane holds 4-feature
+  // pieces of its row spread over the whole row, so stores straight from the
+  // accumulator write 16 bytes into each of 32 rows per instruction (32 cache
+  // lines). Each wave writes its 32 rows to LDS row-major (rows padded by 16
+  // bytes, which spreads a column over the banks) and reads them back as whole
+  // 16-byte chunks: every store instruction then writes 1 KB of consecutive
+  // rows. The region is the wave's own, so only the rings' last readers must
+  // be done (SPLIT == 1: a barrier; SPLIT == 2: the region lies past the
+  // exchange area, and group 0 alone is left). The 8-wave, 256-row
+  // workgroups have no room for it and store directly.
+  constexpr int kRowPad = RB + 16;
+  constexpr int kStage = SPLIT == 2 ? (NW * (3 + 16 * DB) * 64 * 4 + 1023) / 1024 * 1024 : 0;
+  constexpr bool kStaged = kStage + NW * 32 * kRowPad <= SPLIT * 2 * NBUF * kTile;
+  if constexpr (kStaged) {
+    // (the lane's position recomputed here, so that nothing derived from it
+    // stays live through the loop for the epilogue's sake)
+    const int lane_e = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    const int l32_e = lane_e & 31, g_e = lane_e >> 5;
+    const int q_row_e = qt * BR + wave * 32 + l32_e;
+    constexpr int CPR = RB / 16;  // 16-byte chunks per row
+    char* const ostage = smem + kStage + wave * 32 * kRowPad;
+    if constexpr (SPLIT == 1) __syncthreads();
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        u32x2 w;
+        w[0] = Mfma<E>::pack2(acc[db][i * 4 + 0] * inv, acc[db][i * 4 + 1] * inv);
+        w[1] = Mfma<E>::pack2(acc[db][i * 4 + 2] * inv, acc[db][i * 4 + 3] * inv);
+        *reinterpret_cast<u32x2*>(ostage + l32_e * kRowPad + (db * 32 + i * 8 + g_e * 4) * 2) = w;
+      }
+    const int row0 = qt * BR + wave * 32;
+    char* const o0 = p.o + head + (int64_t)row0 * RB;
+#pragma unroll
+    for (int k = 0; k < 32 * RB / 1024; ++k) {
+      const int r = k * (1024 / RB) + lane_e / CPR, ch = lane_e % CPR;
+      const u32x4 w = *reinterpret_cast<const u32x4*>(ostage + r * kRowPad + ch * 16);
+      if (row0 + r < N) *reinterpret_cast<u32x4*>(o0 + r * RB + ch * 16) = w;
+    }
+    if (q_row_e < N && g_e == 0 && p.lse) p.lse[(int64_t)bh * N + q_row_e] = (m_run + log2f(l_tot)) * kLn2;
+  } else if (q_row < N) {
     char* orow = p.o + head + (int64_t)q_row * RB;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
