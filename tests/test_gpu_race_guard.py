@@ -72,11 +72,12 @@ def test_race_guard_long_context_head(poison):
     assert_close(o_h, lse_h, o_ref, lse_ref, w.dtype, "race guard n32768 head 7")
 
 
+@pytest.mark.parametrize("d", [128, 64])
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
 @pytest.mark.parametrize("shape", list(LAUNCH_SHAPES))
-def test_race_guard_launch_shapes(poison, shape, dtype):
+def test_race_guard_launch_shapes(poison, shape, dtype, d):
     B, H, N = LAUNCH_SHAPES[shape]
-    w = Workload(f"guard-{shape}", B, H, N, 128, dtype, 190 + N % 7, 2.0)
+    w = Workload(f"guard-{shape}", B, H, N, d, dtype, 190 + N % 7, 2.0)
     q, k, v = make_inputs(w)
     tq, tk, tv = dev(q, dtype), dev(k, dtype), dev(v, dtype)
     edges = [0, 31, 32, 127, 128, 255, 256, N - 33, N - 32, N - 2, N - 1]
@@ -84,7 +85,7 @@ def test_race_guard_launch_shapes(poison, shape, dtype):
     for scale in (w.scale, -0.6 * w.scale):
         s = float(np.float32(scale))
         for causal in (False, True):
-            what = f"race guard {shape} B{B} H{H} N{N} {dtype} scale={s:+.4f} causal={causal}"
+            what = f"race guard {shape} B{B} H{H} N{N} d{d} {dtype} scale={s:+.4f} causal={causal}"
             print(f"[race-guard] {what}", flush=True)
             o, lse = fa.flash_attn_fwd(tq, tk, tv, s, causal=causal)
             torch.cuda.synchronize()
