@@ -290,6 +290,7 @@ void flash_fwd_half(FwdParams p) {
   // whole tiles of every group, counted from its start
   const int full_all = SPLIT == 1 ? min(kt_end, n_full) : min(kt_end - half, n_full - half);
   using F = std::false_type;
+  using T = std::true_type;
   // Ring start: the copies of virtual steps -4..-1 (step t copies K_{t+4} and
   // V_{t+2}, in that order): K0; K1; K2, V0; K3, V1.
   for (int t = -4; t < 0; ++t) {
@@ -396,9 +397,9 @@ void flash_fwd_half(FwdParams p) {
   };
   // Exact maximum of c*s over a tile for this lane's row (both lanes of the
   // pair get the same value); hidden keys are set to `hide` first.
-  auto tile_max = [&](f32x16& s, int key0, bool mask) {
+  auto tile_max = [&](f32x16& s, int key0, bool mask, auto mask_rt) {
     f32x16 one[1] = {s};
-    if (mask) {
+    if (decltype(mask_rt)::value && mask) {
       hide_after(one, key0, key_lim, g, hide);
       s = one[0];
     }
@@ -408,7 +409,7 @@ void flash_fwd_half(FwdParams p) {
   auto softmax_tile = [&](f32x16& s, u32x4(&pf)[2], int key0, bool mask, auto mask_rt) {
     float lt = probs(s, pf, key0, mask, mask_rt);
     if (__any(!(lt <= kSumLimit))) {
-      const float m_new = fmaxf(m_run, tile_max(s, key0, mask));
+      const float m_new = fmaxf(m_run, tile_max(s, key0, mask, mask_rt));
       if constexpr (kRoundedSum) {
         // every lane takes part: lanes 0-15 rescale the sums of queries
         // lane and lane + 16, whose factors lanes lane and lane + 16 hold
@@ -450,7 +451,7 @@ void flash_fwd_half(FwdParams p) {
   if (last >= 0) {
     prefetch_k(kbuf(0));
     scores(kbuf(0), sb[0]);
-    m_run = tile_max(sb[0], kt0 * BC, needs_mask(0));  // the first tile sets m exactly
+    m_run = tile_max(sb[0], kt0 * BC, needs_mask(0), T{});  // the first tile sets m exactly
   }
   prefetch_k(kbuf(1));
   __syncthreads();  // step 0 copies K_4 into K_0's slot, which every wave has now read
@@ -485,7 +486,6 @@ void flash_fwd_half(FwdParams p) {
       vm_wait<0>();
     __syncthreads();
   };
-  using T = std::true_type;
   // run-time steps keep tile t's scores in sb[0] and P_{t-1} in pb[1]
   auto rotate = [&]() {
     sb[0] = sb[1];
