@@ -257,10 +257,12 @@ void flash_fwd_half(FwdParams p) {
   // This lane's query row; rows past the end load row N-1 and are not stored.
   // The query loads are issued before any copy (the scheduling barrier keeps
   // them there), so the copy counts below are the last operations in the
-  // vector-memory queue.
+  // vector-memory queue. With two key groups, both groups' waves at one
+  // position need the same 32 query rows: the rows go through LDS instead
+  // (see copy_q below), loaded once per workgroup and with whole-row copies.
   const int q_row = qt * BR + wave * 32 + l32;
   u32x4 qf[KK];
-  {
+  if constexpr (SPLIT == 1) {
     const int q_ld = q_row < N ? q_row : N - 1;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) qf[kk] = ld_global16(Q + ((int64_t)q_ld * D + kk * 16 + g * 8) * 2);
@@ -291,6 +293,26 @@ void flash_fwd_half(FwdParams p) {
   const int full_all = SPLIT == 1 ? min(kt_end, n_full) : min(kt_end - half, n_full - half);
   using F = std::false_type;
   using T = std::true_type;
+  // Two key groups: the workgroup's NW blocks of 32 query rows are copied
+  // like K tiles (same chunk swizzle, so the K operand offsets read them in
+  // the layout of a direct query load) into the V slots 2 and 3 of the two
+  // groups, which the ring start below leaves empty: block b goes to group
+  // b % 2, slot 2 + b / 2, copied by that group's waves. They are read once
+  // every copy has landed, and step 0 (which refills V slot 2) comes after
+  // one more barrier. Rows past N re-read row N-1, as the direct load does.
+  auto qslot = [&](int b) { return smem + (b % 2) * 2 * NBUF * kTile + (NBUF + 2 + b / 2) * kTile; };
+  if constexpr (SPLIT == 2) {
+    static_assert(NW <= 4, "the query blocks must fit in the free V slots");
+#pragma unroll
+    for (int b = grp; b < NW; b += 2) {
+      const int row0 = min(qt * BR + b * 32, N - 1);
+      const i32x4 rs = buffer_rsrc(Q + (int64_t)row0 * RB, kTile);
+      const uint32_t l0 = lds_addr(qslot(b)) + wave * kPer * 1024;
+      const int last = N - 1 - row0;
+#pragma unroll
+      for (int t = 0; t < kPer; ++t) load_lds16(rs, l0 + t * 1024, min(cp_row[t], last) * RB + cp_k[t]);
+    }
+  }
   // Ring start: the copies of virtual steps -4..-1 (step t copies K_{t+4} and
   // V_{t+2}, in that order): K0; K1; K2, V0; K3, V1.
   for (int t = -4; t < 0; ++t) {
@@ -445,6 +467,10 @@ void flash_fwd_half(FwdParams p) {
   // step wait for the copies it has just issued.
   wait_vmem_all();
   __syncthreads();
+  if constexpr (SPLIT == 2) {
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) qf[kk] = *reinterpret_cast<const u32x4*>(qslot(wave) + k_off[kk]);
+  }
   f32x16 sb[2];
   u32x4 pb[2][2];
   m_run = -INFINITY;
@@ -454,7 +480,7 @@ void flash_fwd_half(FwdParams p) {
     m_run = tile_max(sb[0], kt0 * BC, needs_mask(0), T{});  // the first tile sets m exactly
   }
   prefetch_k(kbuf(1));
-  __syncthreads();  // step 0 copies K_4 into K_0's slot, which every wave has now read
+  __syncthreads();  // step 0 copies K_4 into K_0's slot and V_2 into V slot 2, read by every wave by now
 
   // One step. Copies of K_{t+4} and V_{t+2} go out first, into the slots of
   // K_t (last read in step t-1) and V_{t-2} (last read in step t-1). During the
