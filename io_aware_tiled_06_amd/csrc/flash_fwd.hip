@@ -126,7 +126,8 @@ __device__ __forceinline__ bool update_max(float m_tile, float& m_run, float& l_
 // A workgroup of NW waves owns NW * 32 query rows; key tiles of BC = 32.
 // Every SIMD runs two waves: of two 4-wave workgroups per CU, or of one
 // 8-wave workgroup (used on large grids: each K/V tile is then copied into
-// LDS once for 256 query rows instead of 128). (Two 32-row blocks per wave
+// LDS once for 256 query rows instead of 128). At d = 64 the one-group
+// kernels fit three 4-wave workgroups per CU (three waves per SIMD). (Two 32-row blocks per wave
 // would halve the LDS reads per product but needs about 460 registers per
 // lane, hence one wave per SIMD; measured slower on MI355X.)
 //
@@ -459,10 +460,11 @@ void flash_fwd_half(FwdParams p) {
   // Tiles that need masking: the ragged last one, and (causal) the diagonal.
   auto needs_mask = [&](int t) { return kt0 + t == n_full || (CAUSAL && kt0 + t == diag); };
 
-  // Wait for the query loads and every prologue copy. The wait is one the
-  // compiler sees (it does not see the copies): it then knows the query
-  // fragments are in registers on every path into the loop, and puts no wait
-  // of its own in front of the loop's score products. Such a wait would
+  // Wait for the query loads (two key groups: the query copies) and every
+  // prologue copy. The wait is one the compiler sees (it does not see the
+  // copies): it then knows the query fragments are in registers on every path
+  // into the loop, and puts no wait of its own in front of the loop's score
+  // products. Such a wait would
   // count this step's K/V copies too (one in-order counter) and make every
   // step wait for the copies it has just issued.
   wait_vmem_all();
