@@ -486,3 +486,87 @@ def test_launch_shapes_both_signs_sampled_rows(shape, dtype, d):
             else:
                 o_ref, lse_ref = attention_reference(q[:, :, rows], k, v, s)
             assert_close(o_s, lse_s, o_ref, lse_ref, dtype, what)
+
+
+# -- random grids across the launch-shape thresholds -----------------------------
+
+def _random_grids(cus, count_per_class=4, seed=2024):
+    """Seeded (B, H, N, d, dtype, causal, scale sign) cases on both sides of the
+    launch-shape thresholds of the half-precision forward pass, relative to
+    the device's CU count: fewer than two 128-row tiles per CU (key split),
+    whole rounds of two tiles per CU, a last round of at most one tile per CU
+    (the 64-row remainder launch, non-causal) or of more, and (d = 128,
+    N >= 8192) at least four rounds of 256-row tiles. N is ragged except
+    where a class needs exact tile counts."""
+    rng = np.random.default_rng(seed)
+    slots = 2 * cus
+    cases = []
+
+    def split_bh(bh):
+        b = 2 if bh % 2 == 0 and rng.random() < 0.5 else 1
+        return b, bh // b
+
+    def common():
+        return int(rng.choice([64, 128])), str(rng.choice(["bf16", "fp16"])), bool(rng.random() < 0.5), \
+            float(rng.choice([1.0, -0.6]))
+
+    for _ in range(count_per_class):  # key split: fewer than `slots` tiles
+        d, dt, causal, sg = common()
+        n = int(rng.integers(1, 3000))
+        per = -(-n // 128)
+        bh = int(rng.integers(1, max(2, (slots - 1) // per + 1)))
+        cases.append(("split", *split_bh(bh), n, d, dt, causal, sg))
+    for _ in range(count_per_class):  # whole rounds: exactly k * slots tiles
+        d, dt, causal, sg = common()
+        per = int(rng.choice([1, 2, 4, 8, 16]))
+        n = int(rng.integers((per - 1) * 128 + 1, per * 128 + 1))
+        bh = slots * int(rng.integers(1, 3)) // per
+        cases.append(("rounds", *split_bh(bh), n, d, dt, causal, sg))
+    for narrow in (True, False):  # a partial last round, of <= cus tiles or more
+        found = 0
+        while found < count_per_class:
+            d, dt, causal, sg = common()
+            n = int(rng.integers(129, 6000))
+            per = -(-n // 128)
+            bh = int(rng.integers(slots // per + 1, 3 * slots // per + 2))
+            rest = (bh * per) % slots
+            if rest == 0 or (rest <= cus) != narrow:
+                continue
+            cases.append(("rest-narrow" if narrow else "rest-wide", *split_bh(bh), n, d, dt,
+                          False if narrow else causal, sg))
+            found += 1
+    for _ in range(count_per_class):  # 256-row workgroups
+        _, dt, causal, sg = common()
+        n = int(rng.integers(8192, 11000))
+        per = -(-n // 256)
+        bh = -(-4 * cus // per) + int(rng.integers(0, 4))
+        cases.append(("wide", *split_bh(bh), n, 128, dt, causal, sg))
+    return cases
+
+
+def test_random_grids_across_launch_thresholds():
+    """Seeded random grids on both sides of every launch-shape threshold (split,
+    whole rounds, 64-row remainder, larger remainder, 256-row workgroups),
+    both element types, d = 64 and 128, both signs of the scale, causal and
+    not: sampled rows of every head, tile edges and the last rows included,
+    against the oracle."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    for i, (cls, B, H, N, d, dtype, causal, sign) in enumerate(_random_grids(cus)):
+        w = Workload(f"grid-{i}", B, H, N, d, dtype, 500 + i, 2.0)
+        s = float(np.float32(sign * w.scale))
+        what = f"random grid {i} ({cls}) B{B} H{H} N{N} d{d} {dtype} scale={s:+.4f} causal={causal}"
+        print(f"[parity] {what}", flush=True)
+        q, k, v = make_inputs(w)
+        tq, tk, tv = dev(q, dtype), dev(k, dtype), dev(v, dtype)
+        edges = [0, 31, 32, 63, 64, 127, 128, 255, 256, N - 33, N - 32, N - 2, N - 1]
+        rows = np.unique(np.concatenate([sample_rows(N, 6, seed=i), [r for r in edges if 0 <= r < N]]))
+        o, lse = fa.flash_attn_fwd(tq, tk, tv, s, causal=causal)
+        torch.cuda.synchronize()
+        o_s = o[:, :, rows].float().cpu().numpy().astype(np.float64)
+        lse_s = lse[:, :, rows].cpu().numpy().astype(np.float64)
+        if causal:
+            o_ref, lse_ref = causal_rows_reference(q, k, v, s, rows)
+        else:
+            o_ref, lse_ref = attention_reference(q[:, :, rows], k, v, s)
+        assert_close(o_s, lse_s, o_ref, lse_ref, dtype, what)
+        del tq, tk, tv, o, lse
