@@ -215,13 +215,13 @@ def test_running_maximum_paths(order, dtype, causal):
     """Scores whose row maximum moves across key tiles, against the oracle.
 
     The kernel rescales only when a tile's probabilities, formed with the
-    running maximum as it stands, would exceed 2^12 per lane.
+    running maximum as it stands, would exceed 2^15 per lane.
     - increasing: key rows scaled by 1 + 3 j / N. The maximum climbs tile by
       tile, and many tiles take the exact maximum and rescale.
     - decreasing: the reverse. The first tile sets the maximum and no later
       tile rescales.
     - spike: one key in the middle scaled by 8. For many rows that key's
-      score jumps far beyond 2^12 over the running maximum.
+      score jumps far beyond 2^15 over the running maximum.
     Rows are rounded to the element type before both sides see them."""
     from io_aware_tiled_06_amd.workloads import round_to_dtype
 
