@@ -37,16 +37,21 @@ namespace {
 
 constexpr float kLazyRescale = 8.0f;  // log2 units
 // Operands of the next step's products read one step early: the first
-// FA_FWD_KP K operands of the score product and the first FA_FWD_VP V^T
-// operands of the P V product (tunable at build time). With the maximum-ILP
-// schedule the build uses, one K and two V^T operands measured fastest at the
-// 10,000 and 32K workloads (about 1 % over two and four; four and five V^T
-// operands, or two to four K operands, were slower).
+// FA_FWD_KP K operands of the score product (FA_FWD_KP_D64 at d = 64) and the
+// first FA_FWD_VP V^T operands of the P V product (tunable at build time).
+// With the maximum-ILP schedule the build uses, two V^T operands measured
+// fastest everywhere (one and three slower by 0.5-3 %). One K operand is
+// fastest at d = 128 (two: 1.4 % slower at 10,000 tokens, the same at 4096
+// and 32K); at d = 64 two are 1.3-2.3 % faster (the 512-token batch, N = 1000,
+// causal).
 #ifndef FA_FWD_VP
 #define FA_FWD_VP 2
 #endif
 #ifndef FA_FWD_KP
 #define FA_FWD_KP 1
+#endif
+#ifndef FA_FWD_KP_D64
+#define FA_FWD_KP_D64 2
 #endif
 
 struct FwdParams {
@@ -352,7 +357,7 @@ void flash_fwd_half(FwdParams p) {
 
   // S^T = K Q^T for one tile (32 keys x 32 queries); its first KP operands
   // were read one step earlier (prefetch_k).
-  constexpr int KP = FA_FWD_KP;
+  constexpr int KP = D == 64 ? FA_FWD_KP_D64 : FA_FWD_KP;
   u32x4 pre_k[KP];
   auto prefetch_k = [&](const char* kb_lds) {
 #pragma unroll
