@@ -125,6 +125,41 @@ def test_race_guard_backward(poison, B, H, N, d, dtype, causal):
     check(tuple(g[:, :hmax] for g in got), ref, f"race guard B{B} H{H} N{N} d{d} {dtype} causal={causal}", dtype)
 
 
+# Many back-to-back launches of the loops whose wait leaves the newest copies
+# in flight: every output bitwise equal to the first launch's and free of NaN.
+# (Short steps give a late copy the least slack: the 512-token batch at d = 64,
+# 16 steps per workgroup; the key split at 4096; the 8-wave launch at B2 H16
+# N = 8192, four rounds of 256-row workgroups.)
+MANY_CASES = [("b32_n512_d64_bf16", False, 300), ("b32_n512_d64_bf16", True, 300),
+              ("n4096_d128_bf16", False, 200), (Workload("guard-wide", 2, 16, 8192, 128, "bf16", 77), False, 20)]
+
+
+@pytest.mark.parametrize("name,causal,reps", MANY_CASES, ids=lambda x: getattr(x, "name", str(x)))
+def test_race_guard_many_launches(poison, name, causal, reps):
+    w = WORKLOADS[name] if isinstance(name, str) else name
+    q, k, v = (dev(x, w.dtype) for x in make_inputs(w))
+    g = torch.Generator(device="cpu").manual_seed(11)
+    do = torch.randn(q.shape, generator=g).to(q.dtype).to(q.device)
+    print(f"[race-guard] {reps} launches of {w.name} causal={causal}", flush=True)
+    o0, lse0 = fa.flash_attn_fwd(q, k, v, w.scale, causal=causal)
+    g0 = fa.flash_attn_bwd(q, k, v, o0, lse0, do, w.scale, causal=causal)
+    o = torch.empty_like(o0)
+    differ = torch.zeros((), dtype=torch.int64, device=q.device)
+    nan = torch.zeros((), dtype=torch.int64, device=q.device)
+    for i in range(reps):
+        _, lse = fa.flash_attn_fwd(q, k, v, w.scale, causal=causal, out=o)
+        differ += ((o != o0).any() | (lse != lse0).any()).long()
+        nan += (torch.isnan(o).any() | torch.isnan(lse).any()).long()
+        if i % 4 == 0:  # the backward pass is slower: a quarter as many
+            gr = fa.flash_attn_bwd(q, k, v, o0, lse0, do, w.scale, causal=causal)
+            differ += torch.stack([(a != b).any() for a, b in zip(gr, g0)]).any().long()
+            nan += torch.stack([torch.isnan(a).any() for a in gr]).any().long()
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(o0).all()) and all(bool(torch.isfinite(x).all()) for x in g0)
+    assert int(nan) == 0, f"{int(nan)} launches with NaN"
+    assert int(differ) == 0, f"{int(differ)} launches differ from the first"
+
+
 def test_race_guard_library_is_the_poison_build(poison):
     """The fixture really switched libraries (both export the same names)."""
     assert fa.lib()._name == fa.POISON_LIB_PATH
