@@ -1,6 +1,6 @@
 """Benchmark of the fused attention forward pass on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--entry flash|naive]
+    python bench.py [--steps K] [--warmup W] [--workload NAME | --shape B,H,N,d,DTYPE] [--entry flash|naive]
 
 One step is one call of the forward pass over the whole workload (every head,
 every query tile): the complete hot path. Inputs are seeded synthetic tensors
@@ -17,10 +17,11 @@ drawn with sigma 3). Prints one JSON line:
   cpu_baseline  the float64 CPU oracle timed on this host on a bounded sample of
              the same workload (whole query rows, about 10 s of work)
 
-The default 1000 timed calls keep the GPU busy for about 8 s at 32K, long
-enough for a utilisation sampler running beside the benchmark to see it.
   also       (default workload only) the kernel time and TFLOP/s of the
              4096-token case (B=1, H=8, d=128, bf16), the metric's other size
+
+The default 1000 timed calls keep the GPU busy for about 8 s at 32K, long
+enough for a utilisation sampler running beside the benchmark to see it.
 """
 from __future__ import annotations
 
@@ -568,6 +569,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20,
                     help="untimed calls first (with --record-traffic: those of the profiled run)")
     ap.add_argument("--workload", default="n32768_d128_bf16")
+    ap.add_argument("--shape", default=None, metavar="B,H,N,d,DTYPE",
+                    help="time this problem instead of a named workload (inputs drawn as the workloads' are, "
+                         "seed 9, unit-variance q and k; no traffic record)")
     ap.add_argument("--entry", choices=["flash", "naive"], default="flash")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward pass (dQ, dK, dV from the forward's O and LSE); FLOPs counted as "
@@ -624,13 +628,17 @@ def main() -> int:
 
     import io_aware_tiled_06_amd as fa
     from io_aware_tiled_06_amd import traffic
-    from io_aware_tiled_06_amd.workloads import WORKLOADS, make_inputs
+    from io_aware_tiled_06_amd.workloads import WORKLOADS, Workload, make_inputs
 
     if not os.path.exists(fa.LIB_PATH):
         import __graft_entry__
 
         __graft_entry__.build()
-    w = WORKLOADS[args.workload]
+    if args.shape:
+        B, H, N, d, dt = args.shape.split(",")
+        w = Workload(f"b{B}_h{H}_n{N}_d{d}_{dt}", int(B), int(H), int(N), int(d), dt, 9)
+    else:
+        w = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     tdt = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}[w.dtype]
     print(f"[bench] {args.entry} {w.name}: generating inputs", file=sys.stderr, flush=True)
