@@ -561,6 +561,22 @@ def bwd_compulsory_bytes(w) -> int:
     return 8 * elems * w.elem_bytes + 3 * 4 * w.B * w.H * w.N
 
 
+def resolve_workload(name: str, shape: str | None):
+    """The named workload, or (shape "B,H,N,d,DTYPE") a problem of that size
+    with the workloads' input recipe, seed 9 and unit-variance q and k."""
+    from io_aware_tiled_06_amd.workloads import WORKLOADS, Workload
+
+    if not shape:
+        return WORKLOADS[name]
+    parts = shape.split(",")
+    if len(parts) != 5:
+        raise ValueError(f"--shape takes B,H,N,d,DTYPE, got {shape!r}")
+    B, H, N, d = (int(x) for x in parts[:4])
+    if min(B, H, N, d) < 1:
+        raise ValueError(f"--shape sizes must be positive, got {shape!r}")
+    return Workload(f"b{B}_h{H}_n{N}_d{d}_{parts[4]}", B, H, N, d, parts[4], 9)
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -628,17 +644,13 @@ def main() -> int:
 
     import io_aware_tiled_06_amd as fa
     from io_aware_tiled_06_amd import traffic
-    from io_aware_tiled_06_amd.workloads import WORKLOADS, Workload, make_inputs
+    from io_aware_tiled_06_amd.workloads import make_inputs
 
     if not os.path.exists(fa.LIB_PATH):
         import __graft_entry__
 
         __graft_entry__.build()
-    if args.shape:
-        B, H, N, d, dt = args.shape.split(",")
-        w = Workload(f"b{B}_h{H}_n{N}_d{d}_{dt}", int(B), int(H), int(N), int(d), dt, 9)
-    else:
-        w = WORKLOADS[args.workload]
+    w = resolve_workload(args.workload, args.shape)
     dev = torch.device("cuda:0")
     tdt = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}[w.dtype]
     print(f"[bench] {args.entry} {w.name}: generating inputs", file=sys.stderr, flush=True)

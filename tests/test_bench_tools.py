@@ -3,10 +3,13 @@
 - the clock sampler reads the driver's sysfs files correctly (a fake sysfs
   tree stands in for the card);
 - the traffic record is computed correctly from rocprofv3 counter files
-  (synthetic files stand in for a profiled run).
+  (synthetic files stand in for a profiled run);
+- `--shape` resolves to a workload of that size, and malformed shapes raise.
 """
 import os
 import time
+
+import pytest
 
 import bench
 
@@ -121,3 +124,14 @@ def test_record_traffic_rejects_uneven_dispatches(tmp_path, monkeypatch):
     cf, cw = _copies(tmp_path)
     with pytest.raises(ValueError):
         bench.record_traffic(f, f, cf, cw, copy_bytes=1 << 20)  # 4 dispatches are not 3 calls
+
+
+def test_resolve_workload_shape_and_name():
+    w = bench.resolve_workload("n32768_d128_bf16", None)
+    assert (w.B, w.H, w.N, w.d, w.dtype) == (1, 16, 32768, 128, "bf16")
+    w = bench.resolve_workload("n32768_d128_bf16", "2,8,4096,64,fp32")
+    assert (w.name, w.B, w.H, w.N, w.d, w.dtype, w.seed, w.qk_sigma) == ("b2_h8_n4096_d64_fp32", 2, 8, 4096, 64,
+                                                                            "fp32", 9, 1.0)
+    for bad in ("1,8,4096,128", "1,8,4096,128,fp64", "0,8,4096,128,bf16", "1,8,x,128,bf16"):
+        with pytest.raises(ValueError):
+            bench.resolve_workload("n32768_d128_bf16", bad)
