@@ -148,16 +148,23 @@ __device__ __forceinline__ bool update_max(float m_tile, float& m_run, float& l_
 // start each step without waiting on LDS.
 //
 // Running maximum: tile t's probabilities are first computed with m as it
-// stands. If every lane's sum of its 16 probabilities is at most 2^15, every
-// probability is at most 2^15 (they are non-negative) and the tile is done:
-// no row maximum is taken. Otherwise (in practice the tiles where a row's
-// scores jump by several units) the tile's exact maximum is found, m, the
-// running sum and the accumulator are rescaled by 2^(m_old - m_new), and the
-// tile's probabilities are recomputed, now at most 1. m therefore never
-// exceeds the running maximum and trails it by a bounded amount; P stays
-// inside the range of fp16 (65504; 2^15 is the largest power of two below
-// it) and bf16. (Limits of 2^8, 2^12, 2^15 measured: each step up made fewer
-// tiles take the maximum, 1-2 % faster at 32K and causal each time.)
+// stands. If every lane's sum of its 16 probabilities is at most a limit L,
+// every probability is at most L (they are non-negative) and the tile is
+// done: no row maximum is taken. Otherwise (the tiles where a row's scores
+// jump far above m) the tile's exact maximum is found, m, the running sums
+// and the accumulator are rescaled by 2^(m_old - m_new), and the tile's
+// probabilities are recomputed, now at most 1. m therefore never exceeds the
+// running maximum and trails it by less than log2(L). A trailing m
+// multiplies every probability of a row by one common factor, shared by
+// numerator and denominator; floating point rounds relative to magnitude,
+// so each probability keeps its relative rounding error, and L only has to
+// keep the numbers in range. fp16: P must stay below 65504, so L = 2^15 (the
+// largest power of two below it). bf16: P has the exponent range of fp32,
+// and L = 2^40 leaves the float32 accumulator sum_j p_j v_j room for
+// N * max|v| up to 2^87. (Limits of 2^8, 2^12 and 2^15
+// measured 1-2 % faster at 32K and causal each step up; 2^40 for bf16 another
+// 1.7 %, 2.7 % causal: on the 32K workload's peaky scores the maximum rarely
+// jumps that far.)
 //
 // Normaliser of O (bf16 inputs): the probabilities enter the P V product
 // rounded to bf16 (8 significant bits), so O is divided by the sum of those
@@ -190,7 +197,7 @@ void flash_fwd_half(FwdParams p) {
   constexpr int DB = D / 32;  // 32-feature blocks of the output
   constexpr int kTile = BC * RB;
   constexpr int kPer = kTile / 1024 / NW;  // 1 KB direct copies per wave per tile
-  constexpr float kSumLimit = 32768.f;     // per lane and tile, see above
+  constexpr float kSumLimit = std::is_same<E, BF16>::value ? 0x1p40f : 32768.f;  // L, per lane and tile
   static_assert(kTile % (1024 * NW) == 0, "a tile must split into 1 KB copies evenly over the waves");
   using Swz = TileSwizzle<D>;
   __shared__ __attribute__((aligned(1024))) char smem[SPLIT * 2 * NBUF * kTile];  // per group: K ring, V ring

@@ -210,27 +210,30 @@ def test_constant_values(dtype):
 
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
-@pytest.mark.parametrize("order", ["increasing", "decreasing", "spike"])
+@pytest.mark.parametrize("order", ["increasing", "decreasing", "spike", "spike64"])
 def test_running_maximum_paths(order, dtype, causal):
     """Scores whose row maximum moves across key tiles, against the oracle.
 
     The kernel rescales only when a tile's probabilities, formed with the
-    running maximum as it stands, would exceed 2^15 per lane.
+    running maximum as it stands, would exceed a limit per lane: 2^15 for
+    fp16, 2^40 for bf16.
     - increasing: key rows scaled by 1 + 3 j / N. The maximum climbs tile by
-      tile, and many tiles take the exact maximum and rescale.
+      tile (for fp16 many tiles take the exact maximum and rescale).
     - decreasing: the reverse. The first tile sets the maximum and no later
       tile rescales.
     - spike: one key in the middle scaled by 8. For many rows that key's
-      score jumps far beyond 2^15 over the running maximum.
+      score jumps far beyond 2^15 over the running maximum (fp16 rescales).
+    - spike64: the same key scaled by 64, a jump of up to a few hundred in
+      log2 units: beyond 2^40 on about a third of the rows (bf16 rescales).
     Rows are rounded to the element type before both sides see them."""
     from io_aware_tiled_06_amd.workloads import round_to_dtype
 
     w = Workload("rescale", 1, 2, 2048, 128, dtype, 11)
     q, k, v = make_inputs(w)
     n = w.N
-    if order == "spike":
+    if order in ("spike", "spike64"):
         f = np.ones(n, dtype=np.float32)
-        f[n // 2 + 5] = 8.0
+        f[n // 2 + 5] = 8.0 if order == "spike" else 64.0
     else:
         f = 1.0 + 3.0 * np.arange(n, dtype=np.float32) / n
         if order == "decreasing":
