@@ -306,6 +306,124 @@ def time_forward(name: str, steps: int = 20, warmup: int = 5) -> dict:
 COMPARE_WORKLOADS = ("n4096_d128_bf16", "n10000_d128_fp16", "b32_n512_d64_bf16", "n32768_d128_bf16")
 
 
+def phase_clock_summary(recs, event_us: float) -> dict:
+    """Summary of one launch's phase-clock records (8 words each, see
+    FA_DEBUG_CLOCK in flash_fwd.hip): per-workgroup phase times, how many
+    workgroups each CU held and ran in their loops over the launch, the gap
+    between a workgroup's end and the next start on its CU, when the first
+    workgroups of each XCD started, and each XCD's clock and last end. A
+    workgroup's phase boundaries are placed in real time with its own clock
+    (its cycles over its s_memrealtime duration): clocks differ between
+    XCDs and over time."""
+    import collections
+
+    import numpy as np
+
+    a = np.asarray(recs, dtype=np.uint64).reshape(-1, 8)
+    a = a[(a[:, 7] & 0xFF) == 1]
+    r0 = a[:, 0].astype(np.int64)
+    r1 = a[:, 1].astype(np.int64)
+    cyc = a[:, 2:5].astype(np.float64)
+    dur_ns = (r1 - r0) * 10.0  # s_memrealtime runs at 100 MHz
+    ghz = float(cyc[:, 2].sum() / dur_ns.sum())
+    ghz_wg = cyc[:, 2] / np.maximum(dur_ns, 1.0)  # each workgroup's own clock
+    t0 = r0.min()
+    start, end = (r0 - t0) * 10.0, (r1 - t0) * 10.0
+    span = float(end.max())
+    hw = a[:, 5].astype(np.int64)
+    xcc = a[:, 6].astype(np.int64) & 0xF
+    cu = xcc * 256 + ((hw >> 8) & 0xFF)
+    pro, loop_end = cyc[:, 0] / ghz_wg, cyc[:, 1] / ghz_wg  # ns from the workgroup's start
+    grid = np.arange(0.0, span + 20.0, 20.0)
+    resident, in_loop = collections.Counter(), collections.Counter()
+    gaps, last_end = [], []
+    by_cu = collections.defaultdict(list)
+    for i in range(len(a)):
+        by_cu[int(cu[i])].append(i)
+    for idx in by_cu.values():
+        occ = np.zeros(len(grid), dtype=np.int32)
+        lo = np.zeros(len(grid), dtype=np.int32)
+        for i in idx:
+            occ[(grid >= start[i]) & (grid < end[i])] += 1
+            lo[(grid >= start[i] + pro[i]) & (grid < start[i] + loop_end[i])] += 1
+        resident.update(occ.tolist())
+        in_loop.update(lo.tolist())
+        starts = np.sort(start[idx])
+        for e in end[idx]:
+            later = starts[starts >= e - 10.0]
+            if len(later):
+                gaps.append(float(later[0] - e))
+        last_end.append(float(end[idx].max()))
+    per_cu = collections.Counter(len(v) for v in by_cu.values())
+    xcd_first = {int(x): round(float(start[xcc == x].min()) / 1e3, 3) for x in sorted(set(xcc.tolist()))}
+    q = lambda v: [round(float(np.quantile(v, t)) / 1e3, 3) for t in (0.0, 0.5, 1.0)]  # noqa: E731
+    xcd = {int(x): {"clock_ghz": round(float(cyc[xcc == x, 2].sum() / dur_ns[xcc == x].sum()), 3),
+                    "workgroups": int((xcc == x).sum()), "last_end_us": round(float(end[xcc == x].max()) / 1e3, 2)}
+           for x in sorted(set(xcc.tolist()))}
+    tot = sum(resident.values())
+    return {
+        "event_us": round(event_us, 2), "span_us": round(span / 1e3, 2), "workgroups": int(len(a)),
+        "cus": len(by_cu), "workgroups_per_cu": {int(k): v for k, v in sorted(per_cu.items())},
+        "clock_ghz": round(ghz, 3),
+        "prologue_us_min_median_max": q(pro), "loop_us_min_median_max": q(loop_end - pro),
+        "epilogue_us_min_median_max": q(dur_ns - loop_end),
+        "share_with_k_resident": {int(k): round(v / tot, 3) for k, v in sorted(resident.items())},
+        "share_with_k_in_loop": {int(k): round(v / tot, 3) for k, v in sorted(in_loop.items())},
+        "gap_end_to_next_start_us_median": round(float(np.median(gaps)) / 1e3, 3) if gaps else None,
+        "cu_last_end_us_min_median_max": q(np.asarray(last_end)),
+        "xcd_first_start_us": xcd_first,
+        "per_xcd": xcd,
+    }
+
+
+def phase_clock(w, causal: bool, reps: int = 3, warmup: int = 30) -> None:
+    """Run the workload through the phase-clock build and print one JSON line
+    per launch (phase_clock_summary). The build's extra code keeps the
+    kernels' registers and occupancy; its timings are those of the same
+    launch with a few more instructions per workgroup."""
+    import ctypes
+
+    import torch
+
+    import io_aware_tiled_06_amd as fa
+    from io_aware_tiled_06_amd.workloads import make_inputs
+
+    if not os.path.exists(fa.CLOCK_LIB_PATH):
+        from io_aware_tiled_06_amd import build as _b
+
+        _b.build(variant="clock")
+    dev = torch.device("cuda:0")
+    tdt = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}[w.dtype]
+    tq, tk, tv = (torch.from_numpy(x).to(tdt).to(dev) for x in make_inputs(w))
+    o = torch.empty_like(tq)
+    n_max = 65536
+    with fa.using_library(fa.CLOCK_LIB_PATH) as L:
+        L.fa_clock_clear.restype = ctypes.c_int
+        L.fa_clock_read.argtypes = [ctypes.POINTER(ctypes.c_ulonglong), ctypes.c_int]
+        L.fa_clock_read.restype = ctypes.c_int
+        for _ in range(warmup):
+            fa.flash_attn_fwd(tq, tk, tv, w.scale, causal=causal, out=o)
+        buf = (ctypes.c_ulonglong * (8 * n_max))()
+        stream = torch.cuda.current_stream(dev)
+        for rep in range(reps):
+            for _ in range(5):  # the clock where a stream of calls holds it
+                fa.flash_attn_fwd(tq, tk, tv, w.scale, causal=causal, out=o)
+            torch.cuda.synchronize(dev)
+            if L.fa_clock_clear() != 0:
+                raise RuntimeError("fa_clock_clear failed")
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fa.flash_attn_fwd(tq, tk, tv, w.scale, causal=causal, out=o)
+            e1.record(stream)
+            torch.cuda.synchronize(dev)
+            n = L.fa_clock_read(buf, n_max)
+            if n < 0 or n > n_max:
+                raise RuntimeError(f"fa_clock_read returned {n}")
+            out = phase_clock_summary(list(buf)[:8 * n], e0.elapsed_time(e1) * 1e3)
+            out = {"workload": w.name, "causal": causal, "rep": rep, **out}
+            print(json.dumps(out), flush=True)
+
+
 def compare_paths(steps: int = 20) -> None:
     """The fused and the three-pass path on each half-precision workload: one
     JSON line per (workload, path) with kernel time, TFLOP/s, fraction of the
@@ -605,6 +723,9 @@ def main() -> int:
                     help="only run the fused-versus-three-pass sweep at fixed work (time and memory) and exit")
     ap.add_argument("--crossover-d", type=int, default=128, choices=[64, 128],
                     help="head size of the crossover sweep")
+    ap.add_argument("--phase-clock", action="store_true",
+                    help="only run the phase-clock build (libflashattn_clock.so) on --workload/--shape: per-workgroup "
+                         "phase times, per-CU residency and when each XCD's first workgroups started; then exit")
     ap.add_argument("--compare-paths", action="store_true",
                     help="only time the fused and the three-pass path on the four half-precision workloads and exit")
     ap.add_argument("--collect-counters", metavar="OUT_DIR", default=None,
@@ -633,6 +754,9 @@ def main() -> int:
         return 0
     if args.compare_paths:
         compare_paths()
+        return 0
+    if args.phase_clock:
+        phase_clock(resolve_workload(args.workload, args.shape), args.causal)
         return 0
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the library has no multi-GPU path",

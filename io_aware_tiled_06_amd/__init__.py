@@ -23,6 +23,7 @@ __all__ = [
     "lib",
     "LIB_PATH",
     "POISON_LIB_PATH",
+    "CLOCK_LIB_PATH",
     "using_library",
     "EXPORTED_SYMBOLS",
     "DTYPE_CODE",
@@ -43,6 +44,10 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libflashatt
 # The race-guard build of the same sources (every LDS slot a copy refills
 # holds NaN until the copy lands); see using_library().
 POISON_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libflashattn_poison.so")
+# The phase-clock build (the forward kernel records each workgroup's phase
+# times and CU; it also exports fa_clock_clear and fa_clock_read); for
+# bench.py --phase-clock.
+CLOCK_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libflashattn_clock.so")
 EXPORTED_SYMBOLS = ("flash_attn_fwd", "flash_attn_fwd_causal", "flash_attn_bwd", "flash_attn_bwd_causal",
                     "flash_attn_bwd_noalloc", "attn_naive_workspace_bytes", "attn_naive_fwd", "fa_strerror")
 

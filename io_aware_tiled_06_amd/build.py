@@ -2,7 +2,8 @@
 
     python -m io_aware_tiled_06_amd.build            # libflashattn.so
     python -m io_aware_tiled_06_amd.build poison     # libflashattn_poison.so (race guard)
-    python -m io_aware_tiled_06_amd.build all        # both
+    python -m io_aware_tiled_06_amd.build clock      # libflashattn_clock.so (phase clock)
+    python -m io_aware_tiled_06_amd.build all        # all three
 
 Every source is compiled for gfx950 only. The per-kernel register, LDS and
 scratch usage reported by the compiler is written next to the objects
@@ -28,7 +29,12 @@ LIB_PATH = os.path.join(PKG, LIB_NAME)
 # Race-guard variant of the same sources (FA_DEBUG_POISON): every LDS slot a
 # copy refills holds NaN until the copy lands. For tests only; slower.
 POISON_LIB_PATH = os.path.join(PKG, "libflashattn_poison.so")
-VARIANTS = {None: (LIB_PATH, []), "poison": (POISON_LIB_PATH, ["-DFA_DEBUG_POISON"])}
+# Phase-clock variant (FA_DEBUG_CLOCK): the forward kernel records per
+# workgroup when it started, finished its prologue, loop and stores, and on
+# which CU (bench.py --phase-clock). For measurement only.
+CLOCK_LIB_PATH = os.path.join(PKG, "libflashattn_clock.so")
+VARIANTS = {None: (LIB_PATH, []), "poison": (POISON_LIB_PATH, ["-DFA_DEBUG_POISON"]),
+            "clock": (CLOCK_LIB_PATH, ["-DFA_DEBUG_CLOCK"])}
 SOURCES = ["api.hip", "flash_fwd.hip", "flash_bwd.hip", "naive.hip"]
 ARCH = "gfx950"
 
@@ -98,8 +104,9 @@ def _check_spills(kernels: dict) -> None:
 
 
 def build(verbose: bool = False, variant=None) -> str:
-    """Compile all sources and link the shared library (variant None) or the
-    race-guard library (variant "poison"); returns its path."""
+    """Compile all sources and link the shared library (variant None), the
+    race-guard library (variant "poison") or the phase-clock library (variant
+    "clock"); returns its path."""
     os.makedirs(BUILD, exist_ok=True)
     lib_path = VARIANTS[variant][0]
     with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
@@ -113,7 +120,7 @@ def build(verbose: bool = False, variant=None) -> str:
     if not kernels:
         raise RuntimeError("no kernel-resource-usage remarks found in the compiler output")
     if variant is None:
-        _check_spills(kernels)  # the race-guard build may spill (its extra stores); it is for tests only
+        _check_spills(kernels)  # the race-guard and clock builds may spill (their extra code); not the product
     with open(os.path.join(BUILD, f"resource_summary{tag}.txt"), "w") as f:
         for name, v in sorted(kernels.items()):
             f.write(f"{name} VGPRs={v.get('VGPRs')} AGPRs={v.get('AGPRs')} "
@@ -131,9 +138,10 @@ def build(verbose: bool = False, variant=None) -> str:
 
 
 def build_all(verbose: bool = False) -> None:
-    """The library and its race-guard variant."""
+    """The library, its race-guard variant and its phase-clock variant."""
     build(verbose)
     build(verbose, "poison")
+    build(verbose, "clock")
 
 
 if __name__ == "__main__":

@@ -33,6 +33,21 @@
 
 namespace fa {
 
+#ifdef FA_DEBUG_CLOCK
+// Phase-clock build (libflashattn_clock.so, for measurement only; the
+// library proper has none of this). Wave 0 of every workgroup of
+// flash_fwd_half appends one record of eight 64-bit words, taking its slot
+// from a counter: s_memrealtime (100 MHz) at its start and at its end; the
+// s_memtime cycles from its start to the end of its prologue (the first
+// copies landed), to the end of its loop and to the end of its stores; the
+// HW_ID and XCC_ID registers (the CU it ran on); and a tag 1 | NW << 8 |
+// SPLIT << 16 | D << 24 | block << 32. fa_clock_clear and fa_clock_read
+// (below) reset and read them.
+constexpr int kClockMaxRecords = 65536;
+__device__ unsigned long long fa_clock_records[8 * kClockMaxRecords];
+__device__ unsigned int fa_clock_count;
+#endif
+
 namespace {
 
 constexpr float kLazyRescale = 8.0f;  // log2 units
@@ -202,6 +217,9 @@ void flash_fwd_half(FwdParams p) {
   using Swz = TileSwizzle<D>;
   __shared__ __attribute__((aligned(1024))) char smem[SPLIT * 2 * NBUF * kTile];  // per group: K ring, V ring
 
+#ifdef FA_DEBUG_CLOCK
+  const unsigned long long clk_t0 = __builtin_amdgcn_s_memtime(), clk_r0 = __builtin_amdgcn_s_memrealtime();
+#endif
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave_id = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = SPLIT == 1 ? 0 : wave_id / NW;         // key group
@@ -482,6 +500,9 @@ void flash_fwd_half(FwdParams p) {
   // step wait for the copies it has just issued.
   wait_vmem_all();
   __syncthreads();
+#ifdef FA_DEBUG_CLOCK
+  const unsigned long long clk_t1 = __builtin_amdgcn_s_memtime();
+#endif
   if constexpr (SPLIT == 2) {
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) qf[kk] = *reinterpret_cast<const u32x4*>(qslot(wave) + k_off[kk]);
@@ -574,6 +595,9 @@ void flash_fwd_half(FwdParams p) {
   // the last barrier).
   if (last >= 0 && last == steps - 1) accumulate(vbuf(last % NBUF), pb[1]);
 
+#ifdef FA_DEBUG_CLOCK
+  const unsigned long long clk_t2 = __builtin_amdgcn_s_memtime();
+#endif
   if constexpr (kRoundedSum) {
     // the whole row's rounded sum, for this lane's query
     const float s0 = __shfl(lr_acc[0], lane & 15), s1 = __shfl(lr_acc[1], lane & 15);
@@ -668,6 +692,25 @@ void flash_fwd_half(FwdParams p) {
       }
     if (g == 0 && p.lse) p.lse[(int64_t)bh * N + q_row] = (m_run + log2f(l_tot)) * kLn2;
   }
+#ifdef FA_DEBUG_CLOCK
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's stores complete
+  const unsigned long long clk_t3 = __builtin_amdgcn_s_memtime();
+  if (wave_id == 0 && lane == 0) {
+    const unsigned slot = atomicAdd(&fa_clock_count, 1u);
+    if (slot < kClockMaxRecords) {
+      unsigned long long* r = fa_clock_records + 8 * (size_t)slot;
+      r[0] = clk_r0;
+      r[1] = __builtin_amdgcn_s_memrealtime();
+      r[2] = clk_t1 - clk_t0;
+      r[3] = clk_t2 - clk_t0;
+      r[4] = clk_t3 - clk_t0;
+      r[5] = __builtin_amdgcn_s_getreg((31 << 11) | 4);   // HW_ID
+      r[6] = __builtin_amdgcn_s_getreg((31 << 11) | 20);  // XCC_ID
+      r[7] = 1ull | (unsigned long long)NW << 8 | (unsigned long long)SPLIT << 16 | (unsigned long long)D << 24 |
+             (unsigned long long)(unsigned)blk << 32;
+    }
+  }
+#endif
 }
 
 // ---------------------------------------------------------------------------
@@ -963,3 +1006,32 @@ hipError_t launch_flash(const AttnArgs& a) { return launch<false>(a); }
 hipError_t launch_flash_causal(const AttnArgs& a) { return launch<true>(a); }
 
 }  // namespace fa
+
+#ifdef FA_DEBUG_CLOCK
+// Phase-clock build only: reset the record counter; copy up to `max_records`
+// records (8 words each) to `host`. Returns the number of records the kernels
+// wrote since the last reset (records past the buffer's 65536 are dropped, so
+// a return value above that means some were lost), or a negative HIP error
+// code. Both calls are synchronous with respect to the device.
+extern "C" int fa_clock_clear() {
+  const unsigned int zero = 0;
+  const hipError_t e = hipMemcpyToSymbol(HIP_SYMBOL(fa::fa_clock_count), &zero, sizeof zero, 0, hipMemcpyHostToDevice);
+  return e == hipSuccess ? 0 : -(int)e;
+}
+
+extern "C" int fa_clock_read(unsigned long long* host, int max_records) {
+  unsigned int n = 0;
+  hipError_t e = hipMemcpyFromSymbol(&n, HIP_SYMBOL(fa::fa_clock_count), sizeof n, 0, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return -(int)e;
+  unsigned int m = n < (unsigned)fa::kClockMaxRecords ? n : (unsigned)fa::kClockMaxRecords;
+  if (max_records < 0) max_records = 0;
+  if (m > (unsigned)max_records) m = (unsigned)max_records;
+  if (m > 0 && host) {
+    e = hipMemcpyFromSymbol(host, HIP_SYMBOL(fa::fa_clock_records), (size_t)m * 8 * sizeof(unsigned long long), 0,
+                            hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return -(int)e;
+  }
+  return (int)n;
+}
+#endif
+

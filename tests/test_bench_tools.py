@@ -135,3 +135,35 @@ def test_resolve_workload_shape_and_name():
     for bad in ("1,8,4096,128", "1,8,4096,128,fp64", "0,8,4096,128,bf16", "1,8,x,128,bf16"):
         with pytest.raises(ValueError):
             bench.resolve_workload("n32768_d128_bf16", bad)
+
+
+def _clock_record(start_ns, end_ns, pro_ns, loop_end_ns, hw, xcc, ghz=2.0, blk=0):
+    tag = 1 | 4 << 8 | 1 << 16 | 128 << 24 | blk << 32
+    return [start_ns // 10, end_ns // 10, int(pro_ns * ghz), int(loop_end_ns * ghz), int((end_ns - start_ns) * ghz),
+            hw, xcc, tag]
+
+
+def test_phase_clock_summary_synthetic():
+    """Two CUs on two XCDs: CU A runs two 1000 ns workgroups with a 100 ns gap
+    between them, CU B one 2100 ns workgroup; every workgroup spends 100 ns
+    in its prologue; the cycle counts say 2 GHz."""
+    cu_a, cu_b = 3 << 8, 5 << 8  # HW_ID CU_ID fields
+    recs = (_clock_record(0, 1000, 100, 900, cu_a, 0, blk=0) + _clock_record(1100, 2100, 100, 900, cu_a, 0, blk=1)
+            + _clock_record(0, 2100, 100, 2000, cu_b, 1, blk=2))
+    s = bench.phase_clock_summary(recs, event_us=3.0)
+    assert s["workgroups"] == 3 and s["cus"] == 2
+    assert s["workgroups_per_cu"] == {1: 1, 2: 1}
+    assert s["clock_ghz"] == pytest.approx(2.0)
+    assert s["span_us"] == pytest.approx(2.1)
+    assert s["prologue_us_min_median_max"] == [0.1, 0.1, 0.1]
+    assert s["loop_us_min_median_max"] == [0.8, 0.8, 1.9]
+    assert s["gap_end_to_next_start_us_median"] == pytest.approx(0.1)
+    assert s["xcd_first_start_us"] == {0: 0.0, 1: 0.0}
+    assert s["cu_last_end_us_min_median_max"] == [2.1, 2.1, 2.1]
+    res, loop = s["share_with_k_resident"], s["share_with_k_in_loop"]
+    assert sum(res.values()) == pytest.approx(1.0, abs=2e-3) and sum(loop.values()) == pytest.approx(1.0, abs=2e-3)
+    # CU A is empty for 100 of its 2100 ns; B always holds one
+    assert res[0] == pytest.approx(100 / 4200, abs=0.01) and res[1] == pytest.approx(4100 / 4200, abs=0.01)
+    assert 2 not in res
+    assert s["per_xcd"] == {0: {"clock_ghz": 2.0, "workgroups": 2, "last_end_us": 2.1},
+                            1: {"clock_ghz": 2.0, "workgroups": 1, "last_end_us": 2.1}}
