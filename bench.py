@@ -163,11 +163,11 @@ def record_traffic(fetch_csv: str, write_csv: str, copy_fetch_csv: str, copy_wri
 class ClockSampler:
     """Samples the GPU's shader clock and board power while the timed loop runs.
 
-    Reads the driver's sysfs files of the one GPU card present: the current
+    Reads the amdgpu kernel driver's sysfs files of the one GPU card present: the current
     shader-clock level (``pp_dpm_sclk``, the line marked ``*``) and the board
     power (hwmon ``power1_input``, microwatts) every ``period`` seconds from a
     host thread. The matrix-core peak assumes the full 2.4 GHz clock; under
-    sustained dense work the card may run slower. The driver's clock figure is
+    sustained dense work the card may run slower. The kernel driver's clock figure is
     the firmware's smoothed value, not a cycle count: it shows the trend, while
     the exact cycles of a launch come from the GRBM_COUNT counter under
     rocprofv3. Gives None where the files are absent or more than one card is
@@ -867,7 +867,7 @@ def main() -> int:
     }
     clock = clk.summary()
     if clock:
-        # driver telemetry only: the firmware's clock figure is a smoothed value;
+        # kernel-driver telemetry only: the firmware's clock figure is a smoothed value;
         # the exact cycles of a launch come from the GRBM_COUNT counter
         line["clock"] = clock
     if args.backward:

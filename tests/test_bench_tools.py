@@ -1,6 +1,6 @@
 """bench.py's host-side tools, on the CPU:
 
-- the clock sampler reads the driver's sysfs files correctly (a fake sysfs
+- the clock sampler reads the amdgpu kernel driver's sysfs files correctly (a fake sysfs
   tree stands in for the card);
 - the traffic record is computed correctly from rocprofv3 counter files
   (synthetic files stand in for a profiled run);
