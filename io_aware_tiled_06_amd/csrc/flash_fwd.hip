@@ -566,13 +566,33 @@ void flash_fwd_half(FwdParams p) {
 #define FA_STEADY_STEP(I)                                                                      \
   step(t + (I), sb[(I) % 2], sb[((I) + 1) % 2], pb[((I) + 1) % 2], pb[(I) % 2],               \
        std::integral_constant<int, ((I) + 1) % NBUF>{}, T{}, F{})
+  // Two 4-wave workgroups share a CU (d = 128, one key group). Measured with
+  // the phase clock, one of them runs ahead, and in the last round of a
+  // launch the other then finishes alone at one wave per SIMD for about a
+  // fifth of the launch. Over the last 30 % of its steps a workgroup lowers
+  // its waves' issue priority in three bands, so that the one behind
+  // catches up and both end together (+0.6 to +3.6 % on such launches; the
+  // CU shares less efficiently between equal priorities, so the gain is
+  // smaller than the time spent alone).
+  constexpr bool kPrioBands = !CAUSAL && D == 128 && NW == 4 && SPLIT == 1;
+  if constexpr (kPrioBands) __builtin_amdgcn_s_setprio(3);
   for (; t + 7 < full_all && t + 4 < steady_end; t += 4) {
+    if constexpr (kPrioBands) {
+      const int rem = steps - t;
+      if (rem * 10 < steps)
+        __builtin_amdgcn_s_setprio(0);
+      else if (rem * 5 < steps)
+        __builtin_amdgcn_s_setprio(1);
+      else if (rem * 10 < 3 * steps)
+        __builtin_amdgcn_s_setprio(2);
+    }
     FA_STEADY_STEP(0);
     FA_STEADY_STEP(1);
     FA_STEADY_STEP(2);
     FA_STEADY_STEP(3);
   }
 #undef FA_STEADY_STEP
+  if constexpr (kPrioBands) __builtin_amdgcn_s_setprio(0);
   // Remaining steps in pairs with the buffers' roles swapped (no register
   // moves), then at most one more. Only the ragged last tile and (causal) a
   // wave's diagonal tile need the mask, so the pairs before the first such
