@@ -4,7 +4,8 @@
   tree stands in for the card);
 - the traffic record is computed correctly from rocprofv3 counter files
   (synthetic files stand in for a profiled run);
-- `--shape` resolves to a workload of that size, and malformed shapes raise.
+- `--shape` resolves to a workload of that size, and malformed shapes raise;
+- `--gpus N` above 1 is refused with a message.
 """
 import os
 import time
@@ -167,3 +168,12 @@ def test_phase_clock_summary_synthetic():
     assert 2 not in res
     assert s["per_xcd"] == {0: {"clock_ghz": 2.0, "workgroups": 2, "last_end_us": 2.1},
                             1: {"clock_ghz": 2.0, "workgroups": 1, "last_end_us": 2.1}}
+
+
+@pytest.mark.parametrize("n", [2, 8])
+def test_more_than_one_gpu_is_refused(n, monkeypatch, capsys):
+    """The library has no multi-GPU path: `--gpus N` above 1 ends with exit
+    status 2 and a message, before any GPU work."""
+    monkeypatch.setattr("sys.argv", ["bench.py", "--gpus", str(n)])
+    assert bench.main() == 2
+    assert "one GPU only" in capsys.readouterr().err
