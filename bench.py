@@ -194,8 +194,25 @@ class ClockSampler:
                         self.cap_w = int(f.read()) / 1e6
                 except (OSError, ValueError):
                     pass
+        self.levels_mhz = self._levels() if self.card else []
         self._stop = threading.Event()
         self._thread = threading.Thread(target=self._run, daemon=True)
+
+    def _levels(self) -> list:
+        """The shader-clock levels the card lists (numbered lines of
+        pp_dpm_sclk, MHz); the highest is its top clock."""
+        import re
+
+        out = []
+        try:
+            with open(os.path.join(self.card, "pp_dpm_sclk")) as f:
+                for ln in f:
+                    m = re.match(r"\s*\d+:\s*(\d+)\s*[Mm]hz", ln)
+                    if m:
+                        out.append(int(m.group(1)))
+        except (OSError, ValueError):
+            pass
+        return out
 
     def _sample(self) -> None:
         import re
@@ -241,6 +258,8 @@ class ClockSampler:
             out["power_w_median"] = round(statistics.median(self.power), 1)
         if self.cap_w:
             out["power_cap_w"] = self.cap_w
+        if self.levels_mhz:
+            out["sclk_top_level_mhz"] = max(self.levels_mhz)
         return out
 
 
@@ -286,13 +305,28 @@ def time_entry(name: str, entry: str = "flash", steps: int = 20, warmup: int = 5
     torch.cuda.synchronize(dev)
     ms = [a.elapsed_time(b) for a, b in ev]
     tflops = traffic.attention_flops(w.B, w.H, w.N, w.d) / (float(np.mean(ms)) * 1e-3) / 1e12
-    out = {"workload": name, "entry": entry, "kernel_ms": round(float(np.mean(ms)), 4),
+    out = {"workload": name, "entry": entry, "cache": cache_label(w), "kernel_ms": round(float(np.mean(ms)), 4),
            "kernel_ms_median": round(float(np.median(ms)), 4), "tflops": round(tflops, 3),
            "frac_of_peak": round(tflops / PEAK_TFLOPS[w.dtype], 4), "steps": steps,
            "workspace_bytes": int(ws.numel()) if ws is not None else 0}
     del ws
     torch.cuda.empty_cache()
     return out
+
+
+INFINITY_CACHE_BYTES = 256 << 20  # MI355X's last-level (MALL) cache
+
+
+def cache_label(w) -> str:
+    """Whether a timed call can run from warm caches: back-to-back calls on
+    inputs and outputs that fit the 256 MB Infinity Cache find them there
+    (no cache flush between calls)."""
+    from io_aware_tiled_06_amd import traffic
+
+    c = traffic.compulsory_bytes(w.B, w.H, w.N, w.d, w.elem_bytes)
+    if c <= INFINITY_CACHE_BYTES:
+        return f"warm: Q, K, V, O and LSE ({c / 1e6:.1f} MB) fit the 256 MB Infinity Cache"
+    return f"cold: Q, K, V, O and LSE ({c / 1e6:.1f} MB) exceed every cache"
 
 
 def time_forward(name: str, steps: int = 20, warmup: int = 5) -> dict:
@@ -482,6 +516,12 @@ def cpu_baseline(w, q, k, v, target_s: float = 10.0):
     t = time.perf_counter() - t0
     rows = n_heads * w.N + rows_last
     flops = 4.0 * rows * w.N * w.d
+    blas = None
+    try:
+        cfg = np.show_config(mode="dicts")
+        blas = cfg["Build Dependencies"]["blas"]["name"]
+    except Exception:  # noqa: BLE001 - informational only
+        pass
     cpu = None
     try:
         with open("/proc/cpuinfo") as f:
@@ -493,6 +533,7 @@ def cpu_baseline(w, q, k, v, target_s: float = 10.0):
         "unit": "TFLOP/s",
         "cores": int(threads),
         "cpu_model": cpu,
+        "blas": blas,
         "seconds": round(t, 2),
         "kind": "oracle",
         "sample": (f"{n_heads} whole head(s) + {rows_last} query rows of the next, each row against all "
@@ -863,6 +904,9 @@ def main() -> int:
         },
         "device": torch.cuda.get_device_name(dev),
         "device_cus": torch.cuda.get_device_properties(dev).multi_processor_count,
+        "device_arch": torch.cuda.get_device_properties(dev).gcnArchName,
+        "device_l2_bytes": torch.cuda.get_device_properties(dev).L2_cache_size,
+        "cache": cache_label(w),
         "peak_formula": "256 CUs x 2.4 GHz x 4096 FLOP/clk/CU (dense bf16/fp16 matrix cores); fp32: 157.3 TFLOP/s",
     }
     clock = clk.summary()

@@ -5,7 +5,8 @@
 - the traffic record is computed correctly from rocprofv3 counter files
   (synthetic files stand in for a profiled run);
 - `--shape` resolves to a workload of that size, and malformed shapes raise;
-- `--gpus N` above 1 is refused with a message.
+- `--gpus N` above 1 is refused with a message;
+- the cache label says which timed calls fit the Infinity Cache.
 """
 import os
 import time
@@ -35,6 +36,7 @@ def test_sampler_reads_marked_level_and_power(tmp_path):
     s = c.summary()
     assert s["sclk_mhz_median"] == 1830 and s["sclk_mhz_min"] == 1830 and s["samples"] >= 1
     assert s["power_w_median"] == 1234.5 and s["power_cap_w"] == 1400.0
+    assert s["sclk_top_level_mhz"] == 2400  # the highest numbered level, not the marked one
 
 
 def test_sampler_marked_dpm_level(tmp_path):
@@ -177,3 +179,13 @@ def test_more_than_one_gpu_is_refused(n, monkeypatch, capsys):
     monkeypatch.setattr("sys.argv", ["bench.py", "--gpus", str(n)])
     assert bench.main() == 2
     assert "one GPU only" in capsys.readouterr().err
+
+
+def test_cache_label():
+    """The 4096- and 10,000-token and 512-token-batch calls fit the 256 MB
+    Infinity Cache (warm across back-to-back calls); the 32K call does not."""
+    from io_aware_tiled_06_amd.workloads import WORKLOADS
+
+    assert bench.cache_label(WORKLOADS["n4096_d128_bf16"]).startswith("warm: Q, K, V, O and LSE (33.7 MB)")
+    assert bench.cache_label(WORKLOADS["b32_n512_d64_bf16"]).startswith("warm")
+    assert bench.cache_label(WORKLOADS["n32768_d128_bf16"]).startswith("cold: Q, K, V, O and LSE (539.0 MB)")
