@@ -15,7 +15,7 @@ drawn with sigma 3). Prints one JSON line:
              `traffic` is the measured HBM bytes per launch from the committed
              rocprofv3 counter summary when it matches the current kernel source
   cpu_baseline  the float64 CPU oracle timed on this host on a bounded sample of
-             the same workload (whole query rows, about 10 s of work)
+             the same workload (whole query rows, about 15 s of work)
 
   also       (default workload only) the kernel time and TFLOP/s of the
              4096-token case (B=1, H=8, d=128, bf16), the metric's other size
@@ -480,7 +480,7 @@ def compare_paths(steps: int = 20) -> None:
             print(json.dumps(rec), flush=True)
 
 
-def cpu_baseline(w, q, k, v, target_s: float = 10.0):
+def cpu_baseline(w, q, k, v, target_s: float = 15.0):
     """Time the float64 oracle for about target_s seconds on whole query rows of
     the workload (head by head)."""
     import numpy as np
